@@ -1,0 +1,68 @@
+"""Run the oracle on a synthetic workload (test infrastructure only).
+
+The KV pools of the large workloads are gigabytes, so the oracle never builds
+them whole: `GeneratedCache` produces the stored code of any slot on demand --
+the generated pool value encoded with the oracle's own codec, unless this
+step's store overwrote the slot.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from synth import workloads as W
+
+from . import attention as A
+
+
+class GeneratedCache:
+    def __init__(self, wl: W.Workload, which: str):
+        self.wl = wl
+        self.which = which
+        self.dtype = wl.kv_dtype
+        self.scale = wl.kv_scale
+        self.page_size = wl.page_size
+        self.overlay: dict = {}
+
+    def store(self, new_values_f32: np.ndarray, slot_mapping) -> None:
+        """Same write rule as attention.store_kv, into the overlay."""
+        enc = A.encode(new_values_f32, self.dtype, self.scale)
+        for i, s in enumerate(np.asarray(slot_mapping, dtype=np.int64)):
+            if s >= 0:
+                self.overlay[int(s)] = enc[i]
+
+    def codes_at(self, slots) -> np.ndarray:
+        slots = np.asarray(slots, dtype=np.int64)
+        base = A.encode(W.pool_values(self.wl, self.which, slots), self.dtype, self.scale)
+        for i, s in enumerate(slots):
+            if int(s) in self.overlay:
+                base[i] = self.overlay[int(s)]
+        return base
+
+    def decode_slots(self, slots) -> np.ndarray:
+        c = self.codes_at(slots)
+        tmp = A.Cache(c[:, None], self.dtype, self.scale)   # [n, 1, Hkv, D]
+        return tmp.decode_slots(np.arange(len(c)))
+
+
+def caches_after_store(wl: W.Workload, slot_mapping=None, new_rows=None):
+    """K and V caches of the workload after this step's store_kv."""
+    kc, vc = GeneratedCache(wl, "k"), GeneratedCache(wl, "v")
+    sm = wl.slot_mapping if slot_mapping is None else slot_mapping
+    rows = np.arange(len(sm)) if new_rows is None else new_rows
+    kc.store(W.new_kv_values(wl, "k", rows), sm)
+    vc.store(W.new_kv_values(wl, "v", rows), sm)
+    return kc, vc
+
+
+def decoded_q(wl: W.Workload) -> np.ndarray:
+    return W.q_values(wl).astype(np.float64)
+
+
+def run(wl: W.Workload, window: int = -1, requests=None, caches=None, q=None):
+    """Oracle out/lse (float64) for the workload, optionally for some requests only."""
+    kc, vc = caches if caches is not None else caches_after_store(wl)
+    qq = decoded_q(wl) if q is None else q
+    return A.paged_attention(qq, kc, vc, wl.qo_indptr, wl.kv_indptr, wl.kv_indices,
+                             wl.last_page_len, wl.num_kv_heads, sm_scale=wl.sm_scale,
+                             causal=wl.causal, window=window, requests=requests)
