@@ -1,0 +1,244 @@
+/*
+ * ak.h -- C ABI of the paged-KV attention library (libak.so) for AMD MI355X (gfx950).
+ *
+ * The library computes one step of batched attention over a paged KV cache:
+ *   1. ak_store_kv  scatters this step's new K/V rows into cache slots;
+ *   2. ak_plan      compiles the ragged batch (CSR page table + query offsets)
+ *                   into a work list and split-KV partition, once per step;
+ *   3. ak_run       runs GQA attention for every layer with that plan (decode
+ *                   and causal extend/prefill in one call), merging split-KV
+ *                   partial states by their log-sum-exp.
+ *
+ * Sources (page title, section):
+ *   - "vLLM attention backend" (pinghaoyang.com.cn): "plan() and run()", "From a
+ *     2-D block table to a CSR page table", "Write the KV first", the worked
+ *     example with requests A/B/C, "Nine invariants".
+ *   - "SGLang attention backend" (pinghaoyang.com.cn): the kv_indptr / kv_indices /
+ *     kv_last_page_len triple, "Why metadata is built once per step",
+ *     "The two forms of extend" (state merge), "Where masks come from".
+ *   - mini-sglang handbook, "GPU attention": "FlashInfer: plan and run" and the CPU
+ *     reference paged attention of "Verify on the CPU".
+ *   - "FlashInfer and the backend abstraction" (mlinterviewnotes.com): "plan()",
+ *     "Fail loudly".
+ *
+ * Conventions shared by every entry point
+ *   - Every call returns ak_status; no exception or abort crosses the ABI.  On
+ *     failure ak_last_error() returns a message for the calling thread.
+ *   - Device pointers are HIP device memory on the current device.  Host pointers
+ *     are ordinary process memory.  The caller owns every buffer it passes; the
+ *     library never frees caller memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Kernels are
+ *     enqueued asynchronously on it; errors detected on the host are returned
+ *     before anything is enqueued.
+ *   - Anything outside the supported set returns AK_ERR_UNSUPPORTED; the library
+ *     never substitutes another method ("Fail loudly").
+ */
+#ifndef AK_H_
+#define AK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  AK_OK = 0,
+  AK_ERR_INVALID_ARG = -1,     /* null pointer, negative size, bad enum value    */
+  AK_ERR_UNSUPPORTED = -2,     /* valid request outside the supported set        */
+  AK_ERR_BAD_INDPTR = -3,      /* an indptr array does not start at 0 or decreases */
+  AK_ERR_BAD_LENGTHS = -4,     /* last_page_len out of [1, B], query longer than KV */
+  AK_ERR_SHAPE_MISMATCH = -5,  /* tensor shapes disagree with each other or the plan */
+  AK_ERR_HIP = -6,             /* a HIP runtime call failed                      */
+  AK_ERR_OOM = -7              /* device or host allocation failed               */
+} ak_status;
+
+typedef enum {
+  AK_F32 = 0,       /* IEEE binary32                                              */
+  AK_BF16 = 1,      /* bfloat16                                                   */
+  AK_FP8_E4M3 = 2,  /* OCP FP8 E4M3 ("fn": no inf, max 448), value = code * scale */
+  AK_I32 = 3,
+  AK_I64 = 4
+} ak_dtype;
+
+/* A strided view of device memory.  shape/stride use the first `ndim` entries;
+ * strides are in elements.  `scale` is read only for AK_FP8_E4M3. */
+typedef struct {
+  void* data;
+  int32_t dtype;     /* ak_dtype */
+  int32_t ndim;
+  int64_t shape[4];
+  int64_t stride[4];
+  float scale;
+} ak_tensor;
+
+/* ------------------------------------------------------------------ store */
+
+/* ak_store_kv -- write this step's K/V into the paged cache by slot.
+ *
+ * Defines ("vLLM attention backend", "Write the KV first"; worked example):
+ * for every new token i with slot_mapping[i] >= 0, flat cache row
+ * slot_mapping[i] (page = slot / B, offset = slot % B) receives k[i] in
+ * k_cache and v[i] in v_cache.  The store is a separate call that must be
+ * enqueued before the ak_run that reads those rows, so decode, extend and
+ * prefill all attend over one cache under a causal bound.
+ *
+ *   k, v          [N, Hkv, D]  F32 or BF16, D contiguous (stride 1).
+ *   slot_mapping  [N]          I64 device array; negative = padding, skipped.
+ *   k_cache,
+ *   v_cache       [P, B, Hkv, D]  F32, BF16 or FP8_E4M3, D contiguous.
+ *
+ * Conversions: equal dtypes copy bits; F32 -> BF16 rounds to nearest even;
+ * F32/BF16 -> FP8_E4M3 computes the binary32 quotient x / cache.scale, rounds it
+ * to nearest even E4M3 and saturates to +-448 (the sign of a zero result is
+ * kept).  BF16 -> F32 and writes into a narrower-than-FP8 type are unsupported.
+ * Every slot must lie in [0, P*B) or be negative; two tokens with the same slot
+ * in one call leave either value (the pages' invariants forbid it).
+ * Errors: AK_ERR_INVALID_ARG (null data, ndim), AK_ERR_SHAPE_MISMATCH (N, Hkv, D
+ * disagree), AK_ERR_UNSUPPORTED (dtype pair), AK_ERR_HIP (launch failure).
+ * N = 0 returns AK_OK and launches nothing. */
+ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v, const ak_tensor* slot_mapping,
+                      ak_tensor* k_cache, ak_tensor* v_cache, void* stream);
+
+/* ------------------------------------------------------------------- plan */
+
+typedef struct ak_plan_t ak_plan_t;    /* opaque; owned by the library */
+
+enum { AK_PLAN_HOST_ONLY = 1 };        /* build the work list without touching the GPU */
+
+typedef struct {
+  float sm_scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim)            */
+  int32_t num_cus;       /* compute units to balance for; 0 = ask the device (256
+                            in host-only plans)                                    */
+  int32_t max_splits;    /* upper bound on KV splits per (request, KV head); 0 = 64 */
+  int32_t min_chunk;     /* smallest KV split in tokens; 0 = library default       */
+  int32_t flags;         /* AK_PLAN_HOST_ONLY                                       */
+  void* stream;          /* stream for the plan's upload; NULL = default stream     */
+} ak_plan_opts;
+
+/* ak_plan -- compile one batch's metadata into a reusable plan.
+ *
+ * Defines ("vLLM attention backend", "plan() and run()" and "From a 2-D block
+ * table to a CSR page table"; "SGLang attention backend", the kv_indptr /
+ * kv_indices / kv_last_page_len triple; mini-sglang "FlashInfer: plan and run"):
+ * request r owns query rows qo_indptr[r] .. qo_indptr[r+1]-1 of q and the pages
+ * kv_indices[kv_indptr[r] .. kv_indptr[r+1]-1]; its KV length is
+ *   L_r = (kv_indptr[r+1] - kv_indptr[r] - 1) * page_size + last_page_len[r]
+ * (0 when it has no pages), and its n_r queries sit at positions L_r - n_r + j.
+ * Query head h reads KV head h / (num_qo_heads / num_kv_heads).
+ *
+ *   qo_indptr      host int32 [batch_size + 1]   (copied)
+ *   kv_indptr      host int32 [batch_size + 1]   (copied)
+ *   kv_indices     DEVICE int32 [kv_indptr[batch_size]]  physical page ids;
+ *                  borrowed, not read by ak_plan: it must stay allocated and
+ *                  unchanged until the last ak_run with this plan.
+ *   last_page_len  host int32 [batch_size]        (copied); in [1, page_size]
+ *                  for a request with pages, ignored for one without.
+ *   causal         1: key t is visible to a query at position p iff t <= p;
+ *                  0: all keys are visible.
+ *   window         -1: none; w >= 0 (causal only): keys t >= p - w stay visible,
+ *                  i.e. w + 1 keys including the query's own position.
+ *   opts           may be NULL.
+ *   plan           receives the new plan.
+ *
+ * The plan reads only host arrays (no device read-back) and makes one
+ * host-to-device copy of its work list.  Supported: num_qo_heads a multiple of
+ * num_kv_heads with a group of 1, 2, 4, 8 or 16; head_dim 64 or 128; page_size
+ * a power of two in [1, 256].  Errors: AK_ERR_INVALID_ARG, AK_ERR_UNSUPPORTED,
+ * AK_ERR_BAD_INDPTR (qo/kv indptr not starting at 0 or decreasing),
+ * AK_ERR_BAD_LENGTHS (last_page_len outside [1, page_size], n_r > L_r, queries
+ * on a request without pages), AK_ERR_OOM, AK_ERR_HIP.  batch_size = 0 or no
+ * query rows gives a valid empty plan. */
+ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                  const int32_t* last_page_len, int32_t batch_size, int32_t num_qo_heads,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                  int32_t window, const ak_plan_opts* opts, ak_plan_t** plan);
+
+/* ak_plan_destroy -- release a plan's host memory and device workspace.
+ * Waits for nothing: the caller must ensure no ak_run using it is still
+ * executing (synchronise the stream first).  NULL is accepted. */
+void ak_plan_destroy(ak_plan_t* plan);
+
+/* -------------------------------------------------------------------- run */
+
+/* ak_run -- attention for one layer with a plan.
+ *
+ * Defines (mini-sglang "Verify on the CPU" reference paged attention; "SGLang
+ * attention backend", "Where masks come from" and "The two forms of extend"):
+ * for query row i of request r at position p and query head h,
+ *   s_t   = sm_scale * q[i,h,:] . K_r[t, h/G, :]   for visible keys t,
+ *   out   = sum_t exp(s_t - m) V_r[t, h/G, :] / sum_t exp(s_t - m),
+ *   lse   = m + ln sum_t exp(s_t - m)              (natural log),
+ * with K_r[t] read from row kv_indices[kv_indptr[r] + t / B] * B + t % B of the
+ * cache.  A (request, KV head) whose keys the plan split into S > 1 parts is
+ * finished by merging the parts' (out, lse) states: m = max lse_s,
+ * out = sum_s e^(lse_s - m) out_s / sum_s e^(lse_s - m).
+ *
+ *   q        [T, Hq, D]   F32 or BF16, T = qo_indptr[batch_size], D contiguous.
+ *   k_cache,
+ *   v_cache  [P, B, Hkv, D] same dtype as q, or FP8_E4M3 with BF16 q (the
+ *            tensors' scale fields are the per-tensor dequantisation scales).
+ *   out      [T, Hq, D]   dtype of q (never FP8), D contiguous; written.
+ *   lse      [T, Hq]      F32, or NULL; written.
+ *
+ * Every row of out/lse that belongs to a request with n_r > 0 is written.
+ * A plan may be run any number of times (once per layer) on one stream; runs
+ * sharing a plan must not overlap in time (they share its split workspace).
+ * Errors: AK_ERR_INVALID_ARG (null plan/tensor, host-only plan),
+ * AK_ERR_SHAPE_MISMATCH (T, Hq, Hkv, D or B disagree with the plan -- a plan
+ * built for fewer heads is rejected, never run), AK_ERR_UNSUPPORTED (dtype
+ * combination, misaligned rows), AK_ERR_HIP.  An empty plan returns AK_OK and
+ * launches nothing. */
+ak_status ak_run(const ak_plan_t* plan, const ak_tensor* q, const ak_tensor* k_cache,
+                 const ak_tensor* v_cache, ak_tensor* out, ak_tensor* lse, void* stream);
+
+/* ----------------------------------------------------------- diagnostics */
+
+/* Thread-local text of the last error (empty string if none).  Owned by the
+ * library; valid until the next ak_* call on the same thread. */
+const char* ak_last_error(void);
+
+/* ak_plan_info -- host-side summary of a plan (any plan, host-only included).
+ * Writes up to 8 int64 values into `info` (caller-owned host array):
+ *   [0] batch_size  [1] total query rows T  [2] work items  [3] small-tile items
+ *   [4] large-tile items  [5] split (request, KV head) units  [6] merge jobs
+ *   [7] partial rows in the split workspace.
+ * Errors: AK_ERR_INVALID_ARG. */
+ak_status ak_plan_info(const ak_plan_t* plan, int64_t* info, int32_t n);
+
+/* ak_plan_export -- copy the plan's work list to host memory for checking.
+ * Each item is 8 int32: request, kv_head, first row, row count, kv_begin,
+ * kv_end, partial base (-1 = writes the output directly), kind (0 small tile,
+ * 1 large tile).  Row rho of (request r, KV head hk) is query token
+ * qo_indptr[r] + rho / G and query head hk*G + rho % G.  Also writes the
+ * per-request KV lengths L_r into `kv_lens` (host int32 [batch_size], may be
+ * NULL).  `items` holds `capacity` items; more than that returns
+ * AK_ERR_INVALID_ARG with the needed count in *count. */
+ak_status ak_plan_export(const ak_plan_t* plan, int32_t* items, int64_t capacity, int64_t* count,
+                         int32_t* kv_lens);
+
+/* ak_gather_slots -- the plan's KV indexing, materialised (debug).
+ * For every request r and position t < L_r writes the flat cache slot the
+ * attention kernels read, kv_indices[kv_indptr[r] + t / B] * B + t % B, into
+ * slots[kv_offset_r + t], where kv_offset_r = sum of L over earlier requests.
+ * `slots` is a device int64 array of at least sum_r L_r entries.  Uses the same
+ * device-side address arithmetic as ak_run.  Errors: AK_ERR_INVALID_ARG, AK_ERR_HIP. */
+ak_status ak_gather_slots(const ak_plan_t* plan, int64_t* slots, void* stream);
+
+/* Per-kernel timing with HIP events on the launch stream (diagnostics).
+ * ak_profile_enable(1) records an event pair around every kernel the library
+ * launches; ak_profile_read copies, per kernel kind (0 store, 1 small-tile
+ * attention, 2 large-tile attention, 3 merge, 4 fp32 attention), the launch
+ * count and the summed milliseconds measured so far into host arrays of
+ * length n, then resets the counters.  Reading synchronises on the events. */
+ak_status ak_profile_enable(int32_t on);
+ak_status ak_profile_read(int64_t* launches, double* total_ms, int32_t n);
+
+/* Library version string. */
+const char* ak_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AK_H_ */

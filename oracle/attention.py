@@ -120,7 +120,7 @@ def attend_one(q, K, V, q_pos, sm_scale, causal, window, kv_range=None):
 
 def paged_attention(q, k_cache: Cache, v_cache: Cache, qo_indptr, kv_indptr, kv_indices,
                     last_page_len, num_kv_heads, sm_scale=None, causal=True, window=-1,
-                    requests=None, kv_range_of=None):
+                    requests=None, kv_range_of=None, rows_of=None):
     """Batched paged attention, request by request.
 
     q: float64 [sum n, Hq, D].  For request r: gather K/V of positions 0..L_r-1
@@ -128,6 +128,8 @@ def paged_attention(q, k_cache: Cache, v_cache: Cache, qo_indptr, kv_indptr, kv_
     and attend with query head h reading KV head h // G.
     `requests` limits the work to some requests (others are left as NaN).
     `kv_range_of(r)` optionally gives a key range per request (split parts).
+    `rows_of(r)` optionally lists which of request r's query indices j to compute
+    (each query row is computed independently of the others).
     Returns out float64 [sum n, Hq, D], lse float64 [sum n, Hq].
     """
     q = np.asarray(q, dtype=np.float64)
@@ -148,14 +150,15 @@ def paged_attention(q, k_cache: Cache, v_cache: Cache, qo_indptr, kv_indptr, kv_
         slots = request_slots(kv_indptr, kv_indices, last_page_len, B, r)
         K = k_cache.decode_slots(slots)                     # [L, Hkv, D]
         V = v_cache.decode_slots(slots)
-        q_pos = L - n + np.arange(n)
+        js = np.arange(n) if rows_of is None else np.asarray(rows_of(r), dtype=np.int64)
+        q_pos = L - n + js
         rng_r = None if kv_range_of is None else kv_range_of(r)
         for h in range(Hq):
             hk = h // G
-            o, l = attend_one(q[q0:q0 + n, h, :], K[:, hk, :], V[:, hk, :], q_pos, scale,
+            o, l = attend_one(q[q0 + js, h, :], K[:, hk, :], V[:, hk, :], q_pos, scale,
                               causal, window, rng_r)
-            out[q0:q0 + n, h, :] = o
-            lse[q0:q0 + n, h] = l
+            out[q0 + js, h, :] = o
+            lse[q0 + js, h] = l
     return out, lse
 
 

@@ -31,8 +31,22 @@ class GeneratedCache:
             if s >= 0:
                 self.overlay[int(s)] = enc[i]
 
+    def materialize(self, slots) -> None:
+        """Generate and keep the codes of these slots, so later reads of them do
+        no input generation (used to time the oracle's own work only)."""
+        slots = np.unique(np.asarray(slots, dtype=np.int64))
+        self._pre_slots = None
+        codes = self.codes_at(slots)
+        self._pre_slots, self._pre_codes = slots, codes
+
     def codes_at(self, slots) -> np.ndarray:
         slots = np.asarray(slots, dtype=np.int64)
+        pre = getattr(self, "_pre_slots", None)
+        if pre is not None:
+            pos = np.searchsorted(pre, slots)
+            pos = np.clip(pos, 0, len(pre) - 1)
+            if np.all(pre[pos] == slots):
+                return self._pre_codes[pos]
         base = A.encode(W.pool_values(self.wl, self.which, slots), self.dtype, self.scale)
         for i, s in enumerate(slots):
             if int(s) in self.overlay:
@@ -59,10 +73,12 @@ def decoded_q(wl: W.Workload) -> np.ndarray:
     return W.q_values(wl).astype(np.float64)
 
 
-def run(wl: W.Workload, window: int = -1, requests=None, caches=None, q=None):
-    """Oracle out/lse (float64) for the workload, optionally for some requests only."""
+def run(wl: W.Workload, window: int = -1, requests=None, caches=None, q=None, rows_of=None):
+    """Oracle out/lse (float64) for the workload, optionally for some requests
+    (and some query rows of them) only; rows not computed are NaN."""
     kc, vc = caches if caches is not None else caches_after_store(wl)
     qq = decoded_q(wl) if q is None else q
     return A.paged_attention(qq, kc, vc, wl.qo_indptr, wl.kv_indptr, wl.kv_indices,
                              wl.last_page_len, wl.num_kv_heads, sm_scale=wl.sm_scale,
-                             causal=wl.causal, window=window, requests=requests)
+                             causal=wl.causal, window=window, requests=requests,
+                             rows_of=rows_of)

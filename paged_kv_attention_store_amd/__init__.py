@@ -1,0 +1,288 @@
+"""Python binding of libak -- batched paged-KV attention on AMD MI355X (gfx950).
+
+A thin ctypes layer over the C ABI in include/ak.h: it marshals torch tensors
+into `ak_tensor` descriptors (data pointer, dtype, shape, strides) and passes the
+current HIP stream.  Every step of the computation runs in libak's kernels;
+torch only provides device memory and streams.  If libak.so is missing or fails
+to load, importing this package raises -- there is no other implementation.
+
+Entry points (same names as the C ABI):
+    ak_store_kv(k, v, slot_mapping, k_cache, v_cache, k_scale=1.0, v_scale=1.0)
+    ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads,
+            num_kv_heads, head_dim, page_size, causal=True, window=-1, ...) -> Plan
+    ak_run(plan, q, k_cache, v_cache, out=None, lse=None, k_scale=1.0, v_scale=1.0)
+    ak_plan_destroy, ak_plan_info, ak_plan_export, ak_gather_slots,
+    ak_profile_enable, ak_profile_read, ak_last_error, ak_version
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libak.so")
+
+# status codes and dtypes, mirroring include/ak.h
+AK_OK = 0
+AK_ERR_INVALID_ARG = -1
+AK_ERR_UNSUPPORTED = -2
+AK_ERR_BAD_INDPTR = -3
+AK_ERR_BAD_LENGTHS = -4
+AK_ERR_SHAPE_MISMATCH = -5
+AK_ERR_HIP = -6
+AK_ERR_OOM = -7
+STATUS_NAMES = {0: "AK_OK", -1: "AK_ERR_INVALID_ARG", -2: "AK_ERR_UNSUPPORTED",
+                -3: "AK_ERR_BAD_INDPTR", -4: "AK_ERR_BAD_LENGTHS", -5: "AK_ERR_SHAPE_MISMATCH",
+                -6: "AK_ERR_HIP", -7: "AK_ERR_OOM"}
+
+AK_F32, AK_BF16, AK_FP8_E4M3, AK_I32, AK_I64 = 0, 1, 2, 3, 4
+AK_PLAN_HOST_ONLY = 1
+
+EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
+            "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
+            "ak_profile_read", "ak_version"]
+
+
+class AkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class AkTensor(ctypes.Structure):
+    _fields_ = [("data", ctypes.c_void_p), ("dtype", ctypes.c_int32), ("ndim", ctypes.c_int32),
+                ("shape", ctypes.c_int64 * 4), ("stride", ctypes.c_int64 * 4),
+                ("scale", ctypes.c_float)]
+
+
+class AkPlanOpts(ctypes.Structure):
+    _fields_ = [("sm_scale", ctypes.c_float), ("num_cus", ctypes.c_int32),
+                ("max_splits", ctypes.c_int32), ("min_chunk", ctypes.c_int32),
+                ("flags", ctypes.c_int32), ("stream", ctypes.c_void_p)]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libak.so not found at {LIB_PATH}; build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    i32p = P(ctypes.c_int32)
+    lib.ak_store_kv.argtypes = [P(AkTensor)] * 5 + [ctypes.c_void_p]
+    lib.ak_store_kv.restype = ctypes.c_int
+    lib.ak_plan.argtypes = [i32p, i32p, ctypes.c_void_p, i32p] + [ctypes.c_int32] * 7 + [
+        P(AkPlanOpts), P(ctypes.c_void_p)]
+    lib.ak_plan.restype = ctypes.c_int
+    lib.ak_plan_destroy.argtypes = [ctypes.c_void_p]
+    lib.ak_plan_destroy.restype = None
+    lib.ak_run.argtypes = [ctypes.c_void_p] + [P(AkTensor)] * 5 + [ctypes.c_void_p]
+    lib.ak_run.restype = ctypes.c_int
+    lib.ak_last_error.argtypes = []
+    lib.ak_last_error.restype = ctypes.c_char_p
+    lib.ak_plan_info.argtypes = [ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_int32]
+    lib.ak_plan_info.restype = ctypes.c_int
+    lib.ak_plan_export.argtypes = [ctypes.c_void_p, i32p, ctypes.c_int64, P(ctypes.c_int64), i32p]
+    lib.ak_plan_export.restype = ctypes.c_int
+    lib.ak_gather_slots.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ak_gather_slots.restype = ctypes.c_int
+    lib.ak_profile_enable.argtypes = [ctypes.c_int32]
+    lib.ak_profile_enable.restype = ctypes.c_int
+    lib.ak_profile_read.argtypes = [P(ctypes.c_int64), P(ctypes.c_double), ctypes.c_int32]
+    lib.ak_profile_read.restype = ctypes.c_int
+    lib.ak_version.argtypes = []
+    lib.ak_version.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def lib():
+    return _lib
+
+
+def ak_last_error() -> str:
+    return _lib.ak_last_error().decode()
+
+
+def ak_version() -> str:
+    return _lib.ak_version().decode()
+
+
+def _check(status: int):
+    if status != AK_OK:
+        raise AkError(status, ak_last_error())
+
+
+# ------------------------------------------------------------ marshalling
+
+def _dtype_code(t) -> int:
+    import torch
+
+    m = {torch.float32: AK_F32, torch.bfloat16: AK_BF16, torch.uint8: AK_FP8_E4M3,
+         torch.float8_e4m3fn: AK_FP8_E4M3, torch.int32: AK_I32, torch.int64: AK_I64}
+    if t.dtype not in m:
+        raise TypeError(f"unsupported tensor dtype {t.dtype}")
+    return m[t.dtype]
+
+
+def tensor_desc(t, scale: float = 1.0) -> AkTensor:
+    """Describe a torch tensor (device memory) for the C ABI."""
+    if t.dim() > 4:
+        raise ValueError("at most 4 dimensions")
+    d = AkTensor()
+    d.data = t.data_ptr() if t.numel() > 0 else None
+    d.dtype = _dtype_code(t)
+    d.ndim = t.dim()
+    for i in range(t.dim()):
+        d.shape[i] = t.shape[i]
+        d.stride[i] = t.stride(i)
+    d.scale = float(scale)
+    return d
+
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        if not torch.cuda.is_available():
+            return ctypes.c_void_p(None)      # host-only paths never launch
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _host_i32(a):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+# ------------------------------------------------------------ entry points
+
+def ak_store_kv(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,
+                stream=None) -> None:
+    """Scatter k/v [N, Hkv, D] into the caches [P, B, Hkv, D] at slot_mapping (int64)."""
+    dk, dv, ds = tensor_desc(k), tensor_desc(v), tensor_desc(slot_mapping)
+    dkc, dvc = tensor_desc(k_cache, k_scale), tensor_desc(v_cache, v_scale)
+    _check(_lib.ak_store_kv(ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(ds),
+                            ctypes.byref(dkc), ctypes.byref(dvc), _stream_ptr(stream)))
+
+
+class Plan:
+    """Owns an ak_plan_t; destroyed with the object (or by ak_plan_destroy)."""
+
+    def __init__(self, handle, num_qo_heads, num_kv_heads, head_dim, page_size, host_only, keep):
+        self.handle = handle
+        self.num_qo_heads = num_qo_heads
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.page_size = page_size
+        self.host_only = host_only
+        self._keep = keep           # the borrowed kv_indices tensor stays alive with the plan
+
+    def __del__(self):
+        ak_plan_destroy(self)
+
+    def info(self) -> dict:
+        return ak_plan_info(self)
+
+
+def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, num_kv_heads: int,
+            head_dim: int, page_size: int, causal: bool = True, window: int = -1,
+            sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
+            min_chunk: int = 0, host_only: bool = False, stream=None) -> Plan:
+    """Build a plan.  qo_indptr, kv_indptr and last_page_len are host arrays
+    (anything NumPy accepts); kv_indices is a device int32 tensor (or None for a
+    host-only plan)."""
+    qo, qo_p = _host_i32(qo_indptr)
+    kv, kv_p = _host_i32(kv_indptr)
+    last, last_p = _host_i32(last_page_len)
+    R = len(qo) - 1
+    if len(kv) != R + 1 or len(last) != R:
+        raise ValueError("qo_indptr/kv_indptr need batch_size+1 entries, last_page_len batch_size")
+    opts = AkPlanOpts()
+    opts.sm_scale = float(sm_scale) if sm_scale else 0.0
+    opts.num_cus = int(num_cus)
+    opts.max_splits = int(max_splits)
+    opts.min_chunk = int(min_chunk)
+    opts.flags = AK_PLAN_HOST_ONLY if host_only else 0
+    opts.stream = None if host_only else _stream_ptr(stream)
+    idx_ptr = None
+    if kv_indices is not None:
+        if not host_only:
+            import torch
+
+            if kv_indices.dtype != torch.int32 or not kv_indices.is_contiguous():
+                raise TypeError("kv_indices must be a contiguous int32 device tensor")
+            idx_ptr = ctypes.c_void_p(kv_indices.data_ptr()) if kv_indices.numel() else None
+    h = ctypes.c_void_p()
+    _check(_lib.ak_plan(qo_p, kv_p, idx_ptr, last_p, R, num_qo_heads, num_kv_heads, head_dim,
+                        page_size, int(bool(causal)), int(window), ctypes.byref(opts),
+                        ctypes.byref(h)))
+    return Plan(h, num_qo_heads, num_kv_heads, head_dim, page_size, host_only, kv_indices)
+
+
+def ak_plan_destroy(plan: Plan) -> None:
+    if plan is not None and plan.handle is not None and plan.handle.value:
+        _lib.ak_plan_destroy(plan.handle)
+        plan.handle = None
+
+
+def ak_run(plan: Plan, q, k_cache, v_cache, out=None, lse=None, k_scale: float = 1.0,
+           v_scale: float = 1.0, stream=None):
+    """Attention for one layer; returns (out, lse).  out/lse are allocated if None
+    (pass them to keep the call allocation-free)."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(q)
+    dq, dk, dv, do = (tensor_desc(q), tensor_desc(k_cache, k_scale), tensor_desc(v_cache, v_scale),
+                      tensor_desc(out))
+    dl = tensor_desc(lse) if lse is not None else None
+    _check(_lib.ak_run(plan.handle, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                       ctypes.byref(do), ctypes.byref(dl) if dl is not None else None,
+                       _stream_ptr(stream)))
+    return out, lse
+
+
+def ak_plan_info(plan: Plan) -> dict:
+    buf = (ctypes.c_int64 * 8)()
+    _check(_lib.ak_plan_info(plan.handle, buf, 8))
+    keys = ["batch_size", "total_q", "items", "small_items", "large_items", "split_units",
+            "merge_jobs", "partial_rows"]
+    return dict(zip(keys, [int(x) for x in buf]))
+
+
+def ak_plan_export(plan: Plan):
+    """Returns (items int32 [n, 8], kv_lens int32 [batch_size])."""
+    info = ak_plan_info(plan)
+    n = info["items"]
+    items = np.zeros((max(n, 1), 8), dtype=np.int32)
+    lens = np.zeros(max(info["batch_size"], 1), dtype=np.int32)
+    cnt = ctypes.c_int64()
+    _check(_lib.ak_plan_export(plan.handle, items.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               n, ctypes.byref(cnt),
+                               lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))))
+    return items[:n], lens[:info["batch_size"]]
+
+
+def ak_gather_slots(plan: Plan, slots, stream=None) -> None:
+    """Write every request's KV slots (device int64 tensor of sum L entries)."""
+    _check(_lib.ak_gather_slots(plan.handle, ctypes.c_void_p(slots.data_ptr()), _stream_ptr(stream)))
+
+
+KERNEL_KINDS = ["store_kv", "attn_small", "attn_large", "merge", "attn_f32"]
+
+
+def ak_profile_enable(on: bool = True) -> None:
+    _check(_lib.ak_profile_enable(int(bool(on))))
+
+
+def ak_profile_read() -> dict:
+    n = len(KERNEL_KINDS)
+    launches = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    _check(_lib.ak_profile_read(launches, ms, n))
+    return {k: (int(launches[i]), float(ms[i])) for i, k in enumerate(KERNEL_KINDS)}

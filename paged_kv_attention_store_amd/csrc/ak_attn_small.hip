@@ -1,0 +1,318 @@
+// Small-tile paged attention: up to 16 query rows of one (request, KV head)
+// against one KV range -- the decode shape (G query heads x n queries <= 16),
+// including one split of a split-KV partition.
+//
+// Method: mini-sglang "GPU attention", CPU reference paged attention (gather
+// K/V through the page list, queries at the sequence end, GQA); "SGLang
+// attention backend", "Where masks come from" (causal bit, window_left) and the
+// head-group fusion figure of "Why metadata is built once per step" (query
+// heads of one KV head share every K/V byte, so they form one tile).
+//
+// gfx950 mapping.  One workgroup (4 waves) per work item; wave w takes the
+// item's 32-token blocks w, w+4, ...  Per block:
+//   S^T (32 tokens x 16 rows) = K (tokens x D) * Q^T   two 16x16x32 bf16 MFMA
+//     tiles per 32 d; K rows go straight from HBM into the MFMA A operand
+//     (each lane loads 32 contiguous bytes of one token row per step pair);
+//   online softmax per row in base 2 (the scale carries log2(e)); a row lives in
+//     the 4 lanes l%16 = row, so its max needs two xor-shuffles;
+//   O^T (D x 16 rows) += V^T * P^T   one 16x16x32 MFMA per 16 d; P stays in the
+//     registers the S^T tile produced it in, V is staged through LDS and read
+//     column-wise.
+// The d order inside a 32-wide k-step is permuted identically for K and Q
+// (contraction order is free), and the token order inside PV's k-steps follows
+// the S^T register layout identically for P and V.
+// The 4 waves' (m, l, O) states are merged in LDS at the end; the item writes
+// the final output or, for a split, its normalised partial and base-2 LSE.
+
+#include "ak_launch.h"
+
+namespace ak {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kBlk = 32;   // tokens per wave block
+
+template <int D>
+__device__ __forceinline__ int dmap(int s, int g4) {
+  // k-step s (0 .. D/32-1), lane group g4 (0..3) -> first of 8 d values
+  return 64 * (s >> 1) + 16 * g4 + 8 * (s & 1);
+}
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+  constexpr int NSTEP = D / 32;       // S^T k-steps
+  constexpr int NDT = D / 16;         // O^T d-tiles
+  constexpr int VROW = D + 4;         // bf16 per staged V row (pad: conflict-free column reads)
+  constexpr int ORW = D + 4;          // floats per row of the combine buffer
+  constexpr int STAGE_BYTES = kWaves * kBlk * VROW * 2;
+  constexpr int COMB_BYTES = (2 * kWaves * 16 + kWaves * 16 * ORW) * 4;
+  constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
+  __shared__ __align__(16) unsigned char smem[SMEM];
+
+  const Item it = a.items[blockIdx.x];
+  const Req rq = a.reqs[it.r];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int n16 = lane & 15;
+  const int g4 = lane >> 4;
+  const int G = a.G;
+
+  // ---- this lane's query row (column of S^T and O^T)
+  const bool rvalid = n16 < it.nrows;
+  const int rho = it.row0 + n16;
+  const int jq = rho / G;
+  const int head = it.hk * G + (rho - jq * G);
+  const int64_t qtok = (int64_t)rq.q_off + jq;
+  const int qpos = rq.L - rq.n + jq;
+  int row_lo = it.kv_begin, row_hi = it.kv_end;
+  if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
+  if (a.causal) row_hi = min(row_hi, qpos + 1);
+  if (!rvalid) row_lo = row_hi = 0;
+
+  bf16x8 qop[NSTEP];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + qtok * a.q_st + (int64_t)head * a.q_sh;
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) {
+      if (rvalid) {
+        qop[s] = *reinterpret_cast<const bf16x8*>(qp + dmap<D>(s, g4));
+      } else {
+        qop[s] = __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+      }
+    }
+  }
+
+  f32x4 oacc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int32_t kv_begin = it.kv_begin, kv_end = it.kv_end;
+  const int nblk = (kv_end - kv_begin + kBlk - 1) / kBlk;
+  const int32_t bmask = (1 << a.log2B) - 1;
+  const int ebytes = FP8 ? 1 : 2;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * ebytes;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * ebytes;
+  __bf16* vs = reinterpret_cast<__bf16*>(smem) + wave * kBlk * VROW;
+
+  for (int b = wave; b < nblk; b += kWaves) {
+    const int tb = kv_begin + b * kBlk;
+    // byte offsets of this block's 32 token rows: lane l computes token tb + (l & 31)
+    int64_t my_koff, my_voff;
+    {
+      const int t = min(tb + (lane & 31), kv_end - 1);
+      const int64_t page = kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
+      const int64_t slot = t & bmask;
+      my_koff = (page * a.k_sp + slot * a.k_sb) * ebytes;
+      my_voff = (page * a.v_sp + slot * a.v_sb) * ebytes;
+    }
+    // ---- K straight into MFMA A-operand registers
+    bf16x8 kop[2][NSTEP];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      const int64_t off = __shfl(my_koff, 16 * T + n16, 64);
+      const char* row = kbase + off;
+#pragma unroll
+      for (int p = 0; p < NSTEP / 2 + (NSTEP == 1); ++p) {
+        const int d0 = 64 * p + 16 * g4;
+        if (FP8) {
+          const u32x4 w = *reinterpret_cast<const u32x4*>(row + d0);
+          kop[T][2 * p] = e4m3x8_to_bf16x8(w[0], w[1]);
+          kop[T][2 * p + 1] = e4m3x8_to_bf16x8(w[2], w[3]);
+        } else {
+          const bf16x8* r = reinterpret_cast<const bf16x8*>(row + d0 * 2);
+          kop[T][2 * p] = r[0];
+          kop[T][2 * p + 1] = r[1];
+        }
+      }
+    }
+    // ---- V rows into LDS (bf16), whole rows per 16-byte chunk
+    {
+      constexpr int CPR = FP8 ? D / 16 : D / 8;   // 16-byte chunks per source row
+      constexpr int TPI = 64 / CPR;               // tokens per load instruction
+      const int c = lane % CPR;
+#pragma unroll
+      for (int i = 0; i < kBlk / TPI; ++i) {
+        const int tt = i * TPI + lane / CPR;
+        const int64_t off = __shfl(my_voff, tt, 64);
+        const u32x4 w = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
+        // staged rows are 8-byte aligned (VROW pad), so write in 8-byte pieces
+        if (FP8) {
+          const u32x4 lo = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[0], w[1]));
+          const u32x4 hi = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[2], w[3]));
+          u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + c * 16);
+          dst[0] = u32x2{lo[0], lo[1]};
+          dst[1] = u32x2{lo[2], lo[3]};
+          dst[2] = u32x2{hi[0], hi[1]};
+          dst[3] = u32x2{hi[2], hi[3]};
+        } else {
+          u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + c * 8);
+          dst[0] = u32x2{w[0], w[1]};
+          dst[1] = u32x2{w[2], w[3]};
+        }
+      }
+    }
+    // ---- S^T = K Q^T
+    f32x4 sacc[2];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      sacc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < NSTEP; ++s) sacc[T] = mfma16(kop[T][s], qop[s], sacc[T]);
+    }
+    // ---- online softmax (base 2), rows = lane % 16
+    float x[2][4];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tb + 16 * T + 4 * g4 + i;
+        const bool vis = (t >= row_lo) & (t < row_hi);
+        x[T][i] = vis ? sacc[T][i] * a.score_scale : -INFINITY;
+        mb = fmaxf(mb, x[T][i]);
+      }
+    mb = fmaxf(mb, shfl_xor_f(mb, 16));
+    mb = fmaxf(mb, shfl_xor_f(mb, 32));
+    const float m_new = fmaxf(m_run, mb);
+    float p[2][4];
+    float alpha = 1.f, psum = 0.f;
+    if (m_new == -INFINITY) {
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p[T][i] = 0.f;
+    } else {
+      alpha = exp2f(m_run - m_new);
+#pragma unroll
+      for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p[T][i] = exp2f(x[T][i] - m_new);
+          psum += p[T][i];
+        }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+    u32x4 pw;
+    pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+    pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+    pw[2] = pack_bf16x2(p[1][0], p[1][1]);
+    pw[3] = pack_bf16x2(p[1][2], p[1][3]);
+    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+    // V staging is private to this wave: wait for its LDS writes (and keep the
+    // compiler from moving LDS accesses across this point)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // ---- O^T += V^T P^T ; k-slot 8*g4 + jj <-> token 16*(jj/4) + 4*g4 + jj%4
+    const uint16_t* vsu = reinterpret_cast<const uint16_t*>(vs);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int d = 16 * dt + n16;
+      u32x4 vw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int jj0 = 2 * h, jj1 = 2 * h + 1;
+        const int t0 = 16 * (jj0 >> 2) + 4 * g4 + (jj0 & 3);
+        const int t1 = 16 * (jj1 >> 2) + 4 * g4 + (jj1 & 3);
+        vw[h] = (uint32_t)vsu[t0 * VROW + d] | ((uint32_t)vsu[t1 * VROW + d] << 16);
+      }
+      oacc[dt] = mfma16(__builtin_bit_cast(bf16x8, vw), pop, oacc[dt]);
+    }
+    // the next block's staging writes must not pass this block's reads
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+
+  // ---- combine the 4 waves' states
+  float l_tot = l_run + shfl_xor_f(l_run, 16);
+  l_tot += shfl_xor_f(l_tot, 32);
+  __syncthreads();
+  float* cm = reinterpret_cast<float*>(smem);
+  float* cl = cm + kWaves * 16;
+  float* co = cl + kWaves * 16;
+  if (g4 == 0) {
+    cm[wave * 16 + n16] = m_run;
+    cl[wave * 16 + n16] = l_tot;
+  }
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) co[(wave * 16 + n16) * ORW + 16 * dt + 4 * g4 + i] = oacc[dt][i];
+  __syncthreads();
+
+  constexpr int CPT = D / 16;   // columns per thread
+  const int row = threadIdx.x >> 4;
+  const int c0 = (threadIdx.x & 15) * CPT;
+  if (row >= it.nrows) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + row]);
+  float o[CPT];
+#pragma unroll
+  for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+  float lse2 = -INFINITY;
+  if (M != -INFINITY) {
+    float den = 0.f;
+    float wt[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      wt[w] = exp2f(cm[w * 16 + row] - M);
+      den += wt[w] * cl[w * 16 + row];
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+#pragma unroll
+      for (int c = 0; c < CPT; ++c) o[c] += wt[w] * co[(w * 16 + row) * ORW + c0 + c];
+    const float inv = a.v_scale / den;
+#pragma unroll
+    for (int c = 0; c < CPT; ++c) o[c] *= inv;
+    lse2 = M + log2f(den);
+  }
+  const int rrho = it.row0 + row;
+  const int rj = rrho / G;
+  const int rhead = it.hk * G + (rrho - rj * G);
+  const int64_t rtok = (int64_t)rq.q_off + rj;
+  if (it.pbase < 0) {
+    uint16_t* op = static_cast<uint16_t*>(a.out) + rtok * a.o_st + (int64_t)rhead * a.o_sh + c0;
+    u32x4 w4;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 2) w4[c / 2] = pack_bf16x2(o[c], o[c + 1]);
+    if (CPT == 8) {
+      *reinterpret_cast<u32x4*>(op) = w4;
+    } else {
+      *reinterpret_cast<u32x2*>(op) = u32x2{w4[0], w4[1]};
+    }
+    if (a.lse && (threadIdx.x & 15) == 0) a.lse[rtok * a.l_st + (int64_t)rhead * a.l_sh] = lse2 * kLn2;
+  } else {
+    const int64_t prow = (int64_t)it.pbase + row;
+    float* pp = a.part_o + prow * D + c0;
+#pragma unroll
+    for (int c = 0; c < CPT; c += 4) *reinterpret_cast<f32x4*>(pp + c) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
+    if ((threadIdx.x & 15) == 0) a.part_lse[prow] = lse2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
+  if (n_items <= 0) return hipSuccess;
+  dim3 grid((unsigned)n_items);
+  if (D == 128 && kv_dtype == AK_BF16) {
+    hipLaunchKernelGGL((attn_small_kernel<128, false>), grid, dim3(256), 0, s, a);
+  } else if (D == 64 && kv_dtype == AK_BF16) {
+    hipLaunchKernelGGL((attn_small_kernel<64, false>), grid, dim3(256), 0, s, a);
+  } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
+    hipLaunchKernelGGL((attn_small_kernel<128, true>), grid, dim3(256), 0, s, a);
+  } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
+    hipLaunchKernelGGL((attn_small_kernel<64, true>), grid, dim3(256), 0, s, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace ak

@@ -1,0 +1,147 @@
+// Device-side helpers for the gfx950 kernels: vector types, number-format
+// conversions, MFMA wrappers and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ak_internal.h"
+
+namespace ak {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ------------------------------------------------------------ conversions
+
+// binary32 -> bfloat16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;   // NaN
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Two bf16 bit patterns (lo, hi) packed in one dword.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Value of an OCP E4M3 ("fn") code as binary32.  Exact: every E4M3 value is a
+// binary32 value.  Built from the fields (bias 7, subnormals m * 2^-9).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xfu;
+  const uint32_t m = c & 7u;
+  float mag;
+  if (e == 0) {
+    mag = (float)m * 0.001953125f;                       // m * 2^-9
+  } else {
+    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  }
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// binary32 value (already divided by the scale) -> E4M3 code: nearest, ties to
+// even, saturating at +-448, sign kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t mag;
+  if (a > 0x7f800000u) {
+    mag = 0x7f;                                          // NaN stays NaN
+  } else if (a >= 0x43e00000u) {                         // |y| >= 448
+    mag = 0x7e;
+  } else if (a < 0x3c800000u) {                          // |y| < 2^-6: subnormal grid m * 2^-9
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);   // 0..8, ties to even
+  } else {
+    const uint32_t e = (a >> 23) - 127u + 7u;           // biased E4M3 exponent, 1..15
+    const uint32_t keep = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xfffffu;
+    mag = (e << 3) | keep;
+    if (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) mag += 1;
+    if (mag > 0x7e) mag = 0x7e;
+  }
+  return mag | sign;
+}
+
+// Eight consecutive E4M3 codes (two dwords) -> eight bf16 (exact) as bf16x8.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w = h ? hi : lo;
+    // f32 of an E4M3 value has at most 4 significant bits: truncating to bf16 is exact.
+    const uint32_t b0 = __float_as_uint(e4m3_to_f32(w & 0xffu)) >> 16;
+    const uint32_t b1 = __float_as_uint(e4m3_to_f32((w >> 8) & 0xffu)) >> 16;
+    const uint32_t b2 = __float_as_uint(e4m3_to_f32((w >> 16) & 0xffu)) >> 16;
+    const uint32_t b3 = __float_as_uint(e4m3_to_f32(w >> 24)) >> 16;
+    r[2 * h] = b0 | (b1 << 16);
+    r[2 * h + 1] = b2 | (b3 << 16);
+  }
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// ------------------------------------------------------------------ MFMA
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%16][8*(l/16) .. +8], B[8*(l/16) .. +8][l%16];
+// D: lane l, element i -> row 4*(l/16) + i, column l%16.
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Lane l holds A[l%32][8*(l/32) .. +8], B[8*(l/32) .. +8][l%32];
+// D: lane l, element i -> row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// ------------------------------------------------------------ reductions
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// --------------------------------------------------------- kernel arguments
+
+struct AttnArgs {
+  const Item* items;
+  const Req* reqs;
+  const int32_t* kv_indices;
+  const void* q;
+  const void* k_cache;
+  const void* v_cache;
+  void* out;
+  float* lse;          // may be null
+  float* part_o;       // [partial_rows, D]
+  float* part_lse;     // [partial_rows], log2 domain
+  int64_t q_st, q_sh;  // q strides (elements): token, head
+  int64_t o_st, o_sh;
+  int64_t l_st, l_sh;
+  int64_t k_sp, k_sb, k_sh;  // cache strides (elements): page, slot, head
+  int64_t v_sp, v_sb, v_sh;
+  int64_t num_pages;   // pages in the pool (page ids are clamped to it)
+  int32_t G, log2B, causal, window;
+  float score_scale;   // sm_scale * log2(e) * k_scale
+  float v_scale;
+};
+
+struct MergeArgs {
+  const MergeJob* jobs;
+  const float* part_o;
+  const float* part_lse;
+  void* out;
+  float* lse;
+  int64_t o_st, o_sh, l_st, l_sh;
+  int32_t n_jobs;
+};
+
+}  // namespace ak

@@ -1,0 +1,86 @@
+// Internal structures shared by the host planner (plain C++) and the HIP runtime.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/ak.h"
+
+namespace ak {
+
+// Rows of one (request, KV head) unit are numbered rho = j * G + g: query token j
+// of the request (position L - n + j), query head hk * G + g.
+
+constexpr int kSmallRows = 16;    // rows of a small (decode-shaped) tile
+constexpr int kLargeRows = 128;   // rows of a large (prefill-shaped) tile
+constexpr int kKvAlign = 64;      // KV split boundaries are multiples of this
+
+struct Item {          // one workgroup's work; 32 bytes
+  int32_t r;           // request
+  int32_t hk;          // KV head
+  int32_t row0;        // first unit row
+  int32_t nrows;       // rows in this tile
+  int32_t kv_begin;    // first KV position
+  int32_t kv_end;      // one past the last KV position
+  int32_t pbase;       // partial row of unit row row0 (-1: write out/lse directly)
+  int32_t kind;        // 0 small tile, 1 large tile
+};
+
+struct Req {           // per request; 16 bytes
+  int32_t q_off;       // first query row in q/out
+  int32_t n;           // query rows
+  int32_t L;           // KV length
+  int32_t page_off;    // kv_indptr[r]
+};
+
+struct MergeJob {      // one (query token, query head) finished from split parts; 32 bytes
+  int32_t token;
+  int32_t head;
+  int32_t pfirst;      // partial row of part 0
+  int32_t pstride;     // distance between consecutive parts' partial rows
+  int32_t count;       // number of parts
+  int32_t pad[3];
+};
+
+}  // namespace ak
+
+struct ak_plan_t {
+  int32_t R = 0, Hq = 0, Hkv = 0, D = 0, B = 0, causal = 1, window = -1, G = 1;
+  int32_t log2B = 0;
+  float sm_scale = 0.f;
+  int64_t T = 0;
+  int32_t num_cus = 256;
+  bool host_only = false;
+  std::vector<int32_t> kv_lens;
+  std::vector<ak::Req> reqs;
+  std::vector<ak::Item> small_items, large_items;
+  std::vector<ak::MergeJob> merges;
+  int64_t partial_rows = 0;
+  int64_t split_units = 0;
+  const int32_t* kv_indices = nullptr;   // device, borrowed
+  int64_t num_kv_pages = 0;
+  // device workspace (one allocation)
+  void* d_buf = nullptr;
+  size_t d_bytes = 0;
+  ak::Req* d_reqs = nullptr;
+  ak::Item* d_small = nullptr;
+  ak::Item* d_large = nullptr;
+  ak::MergeJob* d_merges = nullptr;
+  float* d_part_o = nullptr;
+  float* d_part_lse = nullptr;
+  int device = 0;
+};
+
+namespace ak {
+
+void set_error(const std::string& msg);
+
+// Validates the batch and fills the host side of `p` (everything but the device
+// workspace).  Pure host code: reads only the host arrays.
+ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* last_page_len, int32_t batch_size, int32_t num_qo_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                          int32_t window, const ak_plan_opts* opts, int32_t num_cus, ak_plan_t* p);
+
+}  // namespace ak

@@ -1,0 +1,207 @@
+// Host planner: validation, per-request lengths, tiling and the split-KV
+// partition.  Plain C++ (no HIP): it reads host arrays only, never the device.
+//
+// What a plan holds follows "vLLM attention backend", "plan() and run()" and
+// "FlashInfer and the backend abstraction", "plan()": the batch's ragged
+// structure is turned once per step into a work assignment and split
+// temporaries, which every layer's run reuses.  Lengths follow the CSR section
+// of the vLLM page: L = (pages - 1) * B + last_page_len, last_page_len in [1, B].
+
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <sstream>
+
+#include "ak_internal.h"
+
+namespace ak {
+
+namespace {
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+ak_status fail(ak_status s, const std::string& msg) {
+  set_error(msg);
+  return s;
+}
+
+}  // namespace
+
+ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                          const int32_t* last_page_len, int32_t R, int32_t Hq, int32_t Hkv,
+                          int32_t D, int32_t B, int32_t causal, int32_t window,
+                          const ak_plan_opts* opts, int32_t num_cus, ak_plan_t* p) {
+  if (R < 0) return fail(AK_ERR_INVALID_ARG, "ak_plan: batch_size < 0");
+  if (R > 0 && (!qo_indptr || !kv_indptr || !last_page_len))
+    return fail(AK_ERR_INVALID_ARG, "ak_plan: null indptr or last_page_len array");
+  if (Hq <= 0 || Hkv <= 0 || D <= 0 || B <= 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_plan: head counts, head_dim and page_size must be > 0");
+  if (Hq % Hkv != 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_plan: num_qo_heads is not a multiple of num_kv_heads");
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16)
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan: GQA group size must be 1, 2, 4, 8 or 16");
+  if (D != 64 && D != 128) return fail(AK_ERR_UNSUPPORTED, "ak_plan: head_dim must be 64 or 128");
+  if (!is_pow2(B) || B > 256)
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan: page_size must be a power of two <= 256");
+  if (causal != 0 && causal != 1) return fail(AK_ERR_INVALID_ARG, "ak_plan: causal must be 0 or 1");
+  if (window < -1) return fail(AK_ERR_INVALID_ARG, "ak_plan: window must be -1 or >= 0");
+  if (window >= 0 && !causal)
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan: a sliding window needs causal = 1");
+  if (R > 0 && (qo_indptr[0] != 0 || kv_indptr[0] != 0))
+    return fail(AK_ERR_BAD_INDPTR, "ak_plan: qo_indptr[0] and kv_indptr[0] must be 0");
+
+  p->R = R;
+  p->Hq = Hq;
+  p->Hkv = Hkv;
+  p->D = D;
+  p->B = B;
+  p->G = G;
+  p->log2B = 0;
+  while ((1 << p->log2B) < B) ++p->log2B;
+  p->causal = causal;
+  p->window = window;
+  p->num_cus = num_cus > 0 ? num_cus : 256;
+  p->sm_scale = (opts && opts->sm_scale > 0.f) ? opts->sm_scale : 1.0f / std::sqrt((float)D);
+  const int64_t max_splits = (opts && opts->max_splits > 0) ? opts->max_splits : 64;
+  const int64_t min_chunk =
+      (opts && opts->min_chunk > 0) ? round_up(opts->min_chunk, kKvAlign) : 256;
+
+  // ---- lengths and validation
+  p->kv_lens.assign(R, 0);
+  p->reqs.assign(R, Req{});
+  for (int32_t r = 0; r < R; ++r) {
+    if (qo_indptr[r + 1] < qo_indptr[r] || kv_indptr[r + 1] < kv_indptr[r]) {
+      std::ostringstream os;
+      os << "ak_plan: indptr decreases at request " << r;
+      return fail(AK_ERR_BAD_INDPTR, os.str());
+    }
+  }
+  for (int32_t r = 0; r < R; ++r) {
+    const int64_t pages = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+    const int64_t n = (int64_t)qo_indptr[r + 1] - qo_indptr[r];
+    int64_t L = 0;
+    if (pages > 0) {
+      if (last_page_len[r] < 1 || last_page_len[r] > B) {
+        std::ostringstream os;
+        os << "ak_plan: last_page_len[" << r << "] = " << last_page_len[r] << " outside [1, "
+           << B << "]";
+        return fail(AK_ERR_BAD_LENGTHS, os.str());
+      }
+      L = (pages - 1) * B + last_page_len[r];
+    }
+    if (L > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: KV length exceeds 2^30");
+    if (n > L) {
+      std::ostringstream os;
+      os << "ak_plan: request " << r << " has " << n << " queries but only " << L << " KV tokens";
+      return fail(AK_ERR_BAD_LENGTHS, os.str());
+    }
+    if (n * G > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: too many query rows");
+    p->kv_lens[r] = (int32_t)L;
+    p->reqs[r] = Req{qo_indptr[r], (int32_t)n, (int32_t)L, kv_indptr[r]};
+  }
+  p->T = R > 0 ? qo_indptr[R] : 0;
+  p->num_kv_pages = R > 0 ? kv_indptr[R] : 0;
+
+  // ---- visible KV range of unit rows [a, b)
+  auto kv_range = [&](const Req& q, int64_t a, int64_t b, int32_t& lo, int32_t& hi) {
+    const int64_t pa = (int64_t)q.L - q.n + a / G;          // first row's position
+    const int64_t pb = (int64_t)q.L - q.n + (b - 1) / G;    // last row's position
+    hi = causal ? (int32_t)(pb + 1) : q.L;
+    lo = window >= 0 ? (int32_t)std::max<int64_t>(0, pa - window) : 0;
+  };
+
+  // ---- small units (<= 16 rows) with their split partition
+  struct Unit {
+    int32_t r, hk, rows, lo, hi;
+  };
+  std::vector<Unit> small;
+  int64_t small_tokens = 0;
+  p->small_items.clear();
+  p->large_items.clear();
+  p->merges.clear();
+  for (int32_t r = 0; r < R; ++r) {
+    const Req& q = p->reqs[r];
+    if (q.n == 0) continue;
+    const int64_t rows = (int64_t)q.n * G;
+    if (rows <= kSmallRows) {
+      int32_t lo, hi;
+      kv_range(q, 0, rows, lo, hi);
+      for (int32_t hk = 0; hk < Hkv; ++hk) small.push_back(Unit{r, hk, (int32_t)rows, lo, hi});
+      small_tokens += (int64_t)(hi - lo) * Hkv;
+    } else {
+      for (int64_t row0 = 0; row0 < rows; row0 += kLargeRows) {
+        const int64_t nr = std::min<int64_t>(kLargeRows, rows - row0);
+        int32_t lo, hi;
+        kv_range(q, row0, row0 + nr, lo, hi);
+        for (int32_t hk = 0; hk < Hkv; ++hk)
+          p->large_items.push_back(Item{r, hk, (int32_t)row0, (int32_t)nr, lo, hi, -1, 1});
+      }
+    }
+  }
+
+  // Split size: about eight KV chunks per compute unit over the whole batch,
+  // between min_chunk and 4096 tokens, in multiples of kKvAlign.
+  int64_t chunk = ceil_div(std::max<int64_t>(small_tokens, 1), (int64_t)p->num_cus * 8);
+  chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
+  chunk = std::max<int64_t>(chunk, min_chunk);
+
+  int64_t prow = 0;
+  int64_t split_units = 0;
+  for (const Unit& u : small) {
+    const int64_t len = (int64_t)u.hi - u.lo;
+    int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, chunk)));
+    if (S <= 1) {
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0});
+      continue;
+    }
+    // boundaries on a kKvAlign grid anchored below lo
+    const int64_t base = (u.lo / kKvAlign) * kKvAlign;
+    const int64_t per = round_up(ceil_div((int64_t)u.hi - base, S), kKvAlign);
+    std::vector<std::pair<int32_t, int32_t>> parts;
+    for (int64_t s = 0;; ++s) {
+      const int64_t a = std::max<int64_t>(u.lo, base + s * per);
+      const int64_t b = std::min<int64_t>(u.hi, base + (s + 1) * per);
+      if (a >= u.hi) break;
+      parts.emplace_back((int32_t)a, (int32_t)b);
+    }
+    if (parts.size() == 1) {
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0});
+      continue;
+    }
+    const int64_t ubase = prow;
+    for (size_t s = 0; s < parts.size(); ++s)
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, parts[s].first, parts[s].second,
+                                    (int32_t)(ubase + (int64_t)s * u.rows), 0});
+    const Req& q = p->reqs[u.r];
+    for (int32_t rho = 0; rho < u.rows; ++rho) {
+      MergeJob m{};
+      m.token = q.q_off + rho / G;
+      m.head = u.hk * G + rho % G;
+      m.pfirst = (int32_t)(ubase + rho);
+      m.pstride = u.rows;
+      m.count = (int32_t)parts.size();
+      p->merges.push_back(m);
+    }
+    prow += (int64_t)parts.size() * u.rows;
+    ++split_units;
+    if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
+  }
+  p->partial_rows = prow;
+  p->split_units = split_units;
+
+  // Longest work first, so the tail of the grid holds the short items.
+  std::stable_sort(p->small_items.begin(), p->small_items.end(), [](const Item& a, const Item& b) {
+    return (a.kv_end - a.kv_begin) > (b.kv_end - b.kv_begin);
+  });
+  std::stable_sort(p->large_items.begin(), p->large_items.end(), [](const Item& a, const Item& b) {
+    return (int64_t)a.nrows * (a.kv_end - a.kv_begin) > (int64_t)b.nrows * (b.kv_end - b.kv_begin);
+  });
+  return AK_OK;
+}
+
+}  // namespace ak

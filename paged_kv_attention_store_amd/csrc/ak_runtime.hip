@@ -1,0 +1,529 @@
+// C ABI of libak: argument validation, the plan's device workspace and upload,
+// kernel sequencing for ak_run, diagnostics.  Declarations and contracts are
+// in include/ak.h.
+
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <sstream>
+#include <string>
+#include <vector>
+
+#include "ak_launch.h"
+
+namespace ak {
+
+namespace {
+
+thread_local std::string g_err;
+
+ak_status fail(ak_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+ak_status hip_fail(hipError_t e, const char* where) {
+  std::ostringstream os;
+  os << where << ": " << hipGetErrorString(e);
+  g_err = os.str();
+  return AK_ERR_HIP;
+}
+
+int esize(int dt) {
+  switch (dt) {
+    case AK_F32: return 4;
+    case AK_BF16: return 2;
+    case AK_FP8_E4M3: return 1;
+    case AK_I32: return 4;
+    case AK_I64: return 8;
+    default: return 0;
+  }
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ---------------------------------------------------------------- profiling
+
+enum { kKinds = 5 };
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  int64_t launches[kKinds] = {};
+  double ms[kKinds] = {};
+
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+Profiler g_prof;
+
+struct ProfScope {
+  int kind;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  ProfScope(int k, hipStream_t st) : kind(k), s(st) {
+    if (!g_prof.on) return;
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    a = g_prof.get();
+    b = g_prof.get();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  ~ProfScope() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    g_prof.pending.push_back({kind, a, b});
+  }
+};
+
+int g_cus_cached[64] = {};
+
+int device_cus(int dev) {
+  if (dev >= 0 && dev < 64 && g_cus_cached[dev] > 0) return g_cus_cached[dev];
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus <= 0)
+    cus = 256;
+  if (dev >= 0 && dev < 64) g_cus_cached[dev] = cus;
+  return cus;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+void set_error(const std::string& msg) { g_err = msg; }
+
+}  // namespace ak
+
+using namespace ak;
+
+// ------------------------------------------------------------------- store
+
+extern "C" ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v,
+                                 const ak_tensor* slot_mapping, ak_tensor* k_cache,
+                                 ak_tensor* v_cache, void* stream) {
+  if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+    return fail(AK_ERR_INVALID_ARG, "ak_store_kv: null tensor descriptor");
+  if (k->ndim != 3 || v->ndim != 3 || slot_mapping->ndim != 1 || k_cache->ndim != 4 ||
+      v_cache->ndim != 4)
+    return fail(AK_ERR_INVALID_ARG, "ak_store_kv: expected k/v [N,Hkv,D], slots [N], caches [P,B,Hkv,D]");
+  const int64_t N = k->shape[0], Hkv = k->shape[1], D = k->shape[2];
+  for (int i = 0; i < 3; ++i)
+    if (v->shape[i] != k->shape[i])
+      return fail(AK_ERR_SHAPE_MISMATCH, "ak_store_kv: k and v shapes differ");
+  for (int i = 0; i < 4; ++i)
+    if (v_cache->shape[i] != k_cache->shape[i])
+      return fail(AK_ERR_SHAPE_MISMATCH, "ak_store_kv: k_cache and v_cache shapes differ");
+  if (slot_mapping->shape[0] != N)
+    return fail(AK_ERR_SHAPE_MISMATCH, "ak_store_kv: slot_mapping length differs from N");
+  if (k_cache->shape[2] != Hkv || k_cache->shape[3] != D)
+    return fail(AK_ERR_SHAPE_MISMATCH, "ak_store_kv: cache heads/head_dim differ from k/v");
+  if (slot_mapping->dtype != AK_I64)
+    return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: slot_mapping must be int64");
+  if (k->dtype != v->dtype || k_cache->dtype != v_cache->dtype)
+    return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: k/v (or the two caches) differ in dtype");
+  const int sd = k->dtype, dd = k_cache->dtype;
+  const bool ok_pair = (sd == AK_F32 && (dd == AK_F32 || dd == AK_BF16 || dd == AK_FP8_E4M3)) ||
+                       (sd == AK_BF16 && (dd == AK_BF16 || dd == AK_FP8_E4M3));
+  if (!ok_pair) return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: unsupported dtype conversion");
+  if (N < 0 || Hkv <= 0 || D <= 0 || (D % 8) != 0 || k_cache->shape[1] <= 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_store_kv: bad sizes (head_dim must be a multiple of 8)");
+  if (N == 0) return AK_OK;
+  if (!k->data || !v->data || !slot_mapping->data || !k_cache->data || !v_cache->data)
+    return fail(AK_ERR_INVALID_ARG, "ak_store_kv: null data pointer");
+  if (k->stride[2] != 1 || v->stride[2] != 1 || k_cache->stride[3] != 1 || v_cache->stride[3] != 1 ||
+      slot_mapping->stride[0] != 1)
+    return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: head_dim (and slot_mapping) must be contiguous");
+  const ak_tensor* src[2] = {k, v};
+  const ak_tensor* dst[2] = {k_cache, v_cache};
+  for (int i = 0; i < 2; ++i) {
+    const int64_t sb = esize(sd), db = esize(dd);
+    if (!aligned16(src[i]->data) || !aligned16(dst[i]->data) || (src[i]->stride[0] * sb) % 16 ||
+        (src[i]->stride[1] * sb) % 16 || (dst[i]->stride[0] * db) % 8 || (dst[i]->stride[1] * db) % 8 ||
+        (dst[i]->stride[2] * db) % 8)
+      return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: rows must be 16-byte (source) / 8-byte (cache) aligned");
+    if (dd == AK_FP8_E4M3 && !(dst[i]->scale > 0.f && std::isfinite(dst[i]->scale)))
+      return fail(AK_ERR_INVALID_ARG, "ak_store_kv: fp8 cache needs a positive finite scale");
+  }
+  if (Hkv * (D / 8) > INT32_MAX / 2 || N > INT32_MAX / 2)
+    return fail(AK_ERR_UNSUPPORTED, "ak_store_kv: too many rows");
+  StoreArgs a{};
+  for (int i = 0; i < 2; ++i) {
+    a.src[i] = src[i]->data;
+    a.dst[i] = dst[i]->data;
+    a.s_st[i] = src[i]->stride[0];
+    a.s_sh[i] = src[i]->stride[1];
+    a.d_sp[i] = dst[i]->stride[0];
+    a.d_sb[i] = dst[i]->stride[1];
+    a.d_sh[i] = dst[i]->stride[2];
+    a.scale[i] = dst[i]->scale;
+  }
+  a.slots = static_cast<const int64_t*>(slot_mapping->data);
+  a.num_slots = k_cache->shape[0] * k_cache->shape[1];
+  a.N = (int32_t)N;
+  a.Hkv = (int32_t)Hkv;
+  a.D = (int32_t)D;
+  a.B = (int32_t)k_cache->shape[1];
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope ps(0, s);
+    e = launch_store_kv(a, sd, dd, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ak_store_kv launch");
+  return AK_OK;
+}
+
+// -------------------------------------------------------------------- plan
+
+// The host copy of the uploaded metadata lives as long as the plan, so the
+// asynchronous upload never reads freed memory.
+struct ak_plan_private : ak_plan_t {
+  std::vector<unsigned char> stage;
+};
+
+extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                             const int32_t* kv_indices, const int32_t* last_page_len,
+                             int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t causal, int32_t window,
+                             const ak_plan_opts* opts, ak_plan_t** plan) {
+  if (!plan) return fail(AK_ERR_INVALID_ARG, "ak_plan: null output pointer");
+  *plan = nullptr;
+  const bool host_only = opts && (opts->flags & AK_PLAN_HOST_ONLY);
+  auto* p = new (std::nothrow) ak_plan_private();
+  if (!p) return fail(AK_ERR_OOM, "ak_plan: out of host memory");
+  int dev = 0;
+  int cus = opts && opts->num_cus > 0 ? opts->num_cus : 0;
+  if (!host_only) {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_fail(e, "ak_plan: hipGetDevice");
+    }
+    if (cus == 0) cus = device_cus(dev);
+  }
+  if (cus == 0) cus = 256;
+  ak_status st;
+  try {
+    st = build_plan_host(qo_indptr, kv_indptr, last_page_len, batch_size, num_qo_heads,
+                         num_kv_heads, head_dim, page_size, causal, window, opts, cus, p);
+  } catch (const std::bad_alloc&) {
+    st = fail(AK_ERR_OOM, "ak_plan: out of host memory");
+  }
+  if (st != AK_OK) {
+    delete p;
+    return st;
+  }
+  p->host_only = host_only;
+  p->device = dev;
+  p->kv_indices = kv_indices;
+  if (!host_only && p->num_kv_pages > 0 && !kv_indices) {
+    delete p;
+    return fail(AK_ERR_INVALID_ARG, "ak_plan: null kv_indices with a non-empty page table");
+  }
+  if (!host_only) {
+    const size_t b_req = align256(p->reqs.size() * sizeof(Req));
+    const size_t b_small = align256(p->small_items.size() * sizeof(Item));
+    const size_t b_large = align256(p->large_items.size() * sizeof(Item));
+    const size_t b_merge = align256(p->merges.size() * sizeof(MergeJob));
+    const size_t b_po = align256((size_t)p->partial_rows * p->D * sizeof(float));
+    const size_t b_pl = align256((size_t)p->partial_rows * sizeof(float));
+    const size_t meta = b_req + b_small + b_large + b_merge;
+    p->d_bytes = meta + b_po + b_pl;
+    if (p->d_bytes > 0) {
+      hipError_t e = hipMalloc(&p->d_buf, p->d_bytes);
+      if (e != hipSuccess) {
+        delete p;
+        return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan: device workspace")
+                                        : hip_fail(e, "ak_plan: hipMalloc");
+      }
+      unsigned char* base = static_cast<unsigned char*>(p->d_buf);
+      p->d_reqs = reinterpret_cast<Req*>(base);
+      p->d_small = reinterpret_cast<Item*>(base + b_req);
+      p->d_large = reinterpret_cast<Item*>(base + b_req + b_small);
+      p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
+      p->d_part_o = reinterpret_cast<float*>(base + meta);
+      p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
+      try {
+        p->stage.assign(meta, 0);
+      } catch (const std::bad_alloc&) {
+        (void)hipFree(p->d_buf);
+        delete p;
+        return fail(AK_ERR_OOM, "ak_plan: out of host memory");
+      }
+      unsigned char* h = p->stage.data();
+      if (!p->reqs.empty()) std::memcpy(h, p->reqs.data(), p->reqs.size() * sizeof(Req));
+      if (!p->small_items.empty())
+        std::memcpy(h + b_req, p->small_items.data(), p->small_items.size() * sizeof(Item));
+      if (!p->large_items.empty())
+        std::memcpy(h + b_req + b_small, p->large_items.data(), p->large_items.size() * sizeof(Item));
+      if (!p->merges.empty())
+        std::memcpy(h + b_req + b_small + b_large, p->merges.data(),
+                    p->merges.size() * sizeof(MergeJob));
+      hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+      if (meta > 0) {
+        e = hipMemcpyAsync(p->d_buf, h, meta, hipMemcpyHostToDevice, s);
+        if (e != hipSuccess) {
+          (void)hipFree(p->d_buf);
+          delete p;
+          return hip_fail(e, "ak_plan: upload");
+        }
+      }
+    }
+  }
+  *plan = p;
+  return AK_OK;
+}
+
+extern "C" void ak_plan_destroy(ak_plan_t* plan) {
+  if (!plan) return;
+  if (plan->d_buf) (void)hipFree(plan->d_buf);
+  delete static_cast<ak_plan_private*>(plan);
+}
+
+// --------------------------------------------------------------------- run
+
+extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_tensor* k_cache,
+                            const ak_tensor* v_cache, ak_tensor* out, ak_tensor* lse,
+                            void* stream) {
+  if (!p || !q || !k_cache || !v_cache || !out)
+    return fail(AK_ERR_INVALID_ARG, "ak_run: null plan or tensor descriptor");
+  if (p->host_only) return fail(AK_ERR_INVALID_ARG, "ak_run: plan was built host-only");
+  if (q->ndim != 3 || out->ndim != 3 || k_cache->ndim != 4 || v_cache->ndim != 4 ||
+      (lse && lse->ndim != 2))
+    return fail(AK_ERR_INVALID_ARG, "ak_run: expected q/out [T,Hq,D], caches [P,B,Hkv,D], lse [T,Hq]");
+  if (q->shape[0] != p->T || q->shape[1] != p->Hq || q->shape[2] != p->D) {
+    std::ostringstream os;
+    os << "ak_run: q is [" << q->shape[0] << "," << q->shape[1] << "," << q->shape[2]
+       << "] but the plan expects [" << p->T << "," << p->Hq << "," << p->D << "]";
+    return fail(AK_ERR_SHAPE_MISMATCH, os.str());
+  }
+  for (int i = 0; i < 3; ++i)
+    if (out->shape[i] != q->shape[i]) return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: out shape differs from q");
+  for (int i = 0; i < 4; ++i)
+    if (k_cache->shape[i] != v_cache->shape[i])
+      return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: k_cache and v_cache shapes differ");
+  if (k_cache->shape[1] != p->B || k_cache->shape[2] != p->Hkv || k_cache->shape[3] != p->D)
+    return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: cache page size, KV heads or head_dim differ from the plan");
+  if (lse && (lse->shape[0] != p->T || lse->shape[1] != p->Hq))
+    return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: lse shape differs from [T, Hq]");
+  if (lse && lse->dtype != AK_F32) return fail(AK_ERR_UNSUPPORTED, "ak_run: lse must be float32");
+  if (out->dtype != q->dtype) return fail(AK_ERR_UNSUPPORTED, "ak_run: out dtype must equal q dtype");
+  if (k_cache->dtype != v_cache->dtype)
+    return fail(AK_ERR_UNSUPPORTED, "ak_run: k_cache and v_cache dtypes differ");
+  const int qd = q->dtype, kd = k_cache->dtype;
+  const bool ok = (qd == AK_F32 && kd == AK_F32) ||
+                  (qd == AK_BF16 && (kd == AK_BF16 || kd == AK_FP8_E4M3));
+  if (!ok) return fail(AK_ERR_UNSUPPORTED, "ak_run: supported q/cache dtypes are f32/f32, bf16/bf16, bf16/fp8");
+  if (p->T == 0 || (p->small_items.empty() && p->large_items.empty())) return AK_OK;
+  if (!q->data || !out->data || !k_cache->data || !v_cache->data)
+    return fail(AK_ERR_INVALID_ARG, "ak_run: null data pointer");
+  if (q->stride[2] != 1 || out->stride[2] != 1 || k_cache->stride[3] != 1 || v_cache->stride[3] != 1)
+    return fail(AK_ERR_UNSUPPORTED, "ak_run: head_dim must be contiguous");
+  const int qb = esize(qd), cb = esize(kd);
+  if (!aligned16(q->data) || !aligned16(out->data) || !aligned16(k_cache->data) ||
+      !aligned16(v_cache->data) || (q->stride[0] * qb) % 16 || (q->stride[1] * qb) % 16 ||
+      (out->stride[0] * qb) % 16 || (out->stride[1] * qb) % 16)
+    return fail(AK_ERR_UNSUPPORTED, "ak_run: q/out rows must be 16-byte aligned");
+  for (const ak_tensor* c : {k_cache, v_cache})
+    for (int i = 0; i < 3; ++i)
+      if ((c->stride[i] * cb) % 16) return fail(AK_ERR_UNSUPPORTED, "ak_run: cache rows must be 16-byte aligned");
+  if (kd == AK_FP8_E4M3 && !(k_cache->scale > 0.f && v_cache->scale > 0.f &&
+                             std::isfinite(k_cache->scale) && std::isfinite(v_cache->scale)))
+    return fail(AK_ERR_INVALID_ARG, "ak_run: fp8 caches need positive finite scales");
+
+  AttnArgs a{};
+  a.reqs = p->d_reqs;
+  a.kv_indices = p->kv_indices;
+  a.q = q->data;
+  a.k_cache = k_cache->data;
+  a.v_cache = v_cache->data;
+  a.out = out->data;
+  a.lse = lse ? static_cast<float*>(lse->data) : nullptr;
+  a.part_o = p->d_part_o;
+  a.part_lse = p->d_part_lse;
+  a.q_st = q->stride[0];
+  a.q_sh = q->stride[1];
+  a.o_st = out->stride[0];
+  a.o_sh = out->stride[1];
+  a.l_st = lse ? lse->stride[0] : 0;
+  a.l_sh = lse ? lse->stride[1] : 0;
+  a.k_sp = k_cache->stride[0];
+  a.k_sb = k_cache->stride[1];
+  a.k_sh = k_cache->stride[2];
+  a.v_sp = v_cache->stride[0];
+  a.v_sb = v_cache->stride[1];
+  a.v_sh = v_cache->stride[2];
+  a.num_pages = k_cache->shape[0];
+  a.G = p->G;
+  a.log2B = p->log2B;
+  a.causal = p->causal;
+  a.window = p->window;
+  const float kscale = kd == AK_FP8_E4M3 ? k_cache->scale : 1.f;
+  a.score_scale = p->sm_scale * kLog2e * kscale;
+  a.v_scale = kd == AK_FP8_E4M3 ? v_cache->scale : 1.f;
+  if (a.num_pages <= 0) return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: empty KV pool");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  const int ns = (int)p->small_items.size(), nl = (int)p->large_items.size();
+  if (qd == AK_F32) {
+    a.items = p->d_small;
+    {
+      ProfScope ps(4, s);
+      e = launch_attn_f32(a, ns, p->D, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ak_run: fp32 attention (small items)");
+    a.items = p->d_large;
+    {
+      ProfScope ps(4, s);
+      e = launch_attn_f32(a, nl, p->D, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ak_run: fp32 attention (large items)");
+  } else {
+    if (nl > 0) {
+      a.items = p->d_large;
+      ProfScope ps(2, s);
+      e = launch_attn_large(a, nl, p->D, kd, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ak_run: large-tile attention");
+    if (ns > 0) {
+      a.items = p->d_small;
+      ProfScope ps(1, s);
+      e = launch_attn_small(a, ns, p->D, kd, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ak_run: small-tile attention");
+  }
+  if (!p->merges.empty()) {
+    MergeArgs m{};
+    m.jobs = p->d_merges;
+    m.part_o = p->d_part_o;
+    m.part_lse = p->d_part_lse;
+    m.out = out->data;
+    m.lse = a.lse;
+    m.o_st = a.o_st;
+    m.o_sh = a.o_sh;
+    m.l_st = a.l_st;
+    m.l_sh = a.l_sh;
+    m.n_jobs = (int32_t)p->merges.size();
+    {
+      ProfScope ps(3, s);
+      e = launch_merge(m, p->D, qd, s);
+    }
+    if (e != hipSuccess) return hip_fail(e, "ak_run: merge");
+  }
+  return AK_OK;
+}
+
+// ------------------------------------------------------------- diagnostics
+
+extern "C" const char* ak_last_error(void) { return g_err.c_str(); }
+
+extern "C" ak_status ak_plan_info(const ak_plan_t* p, int64_t* info, int32_t n) {
+  if (!p || !info || n < 0) return fail(AK_ERR_INVALID_ARG, "ak_plan_info: null argument");
+  const int64_t v[8] = {p->R,
+                        p->T,
+                        (int64_t)(p->small_items.size() + p->large_items.size()),
+                        (int64_t)p->small_items.size(),
+                        (int64_t)p->large_items.size(),
+                        p->split_units,
+                        (int64_t)p->merges.size(),
+                        p->partial_rows};
+  for (int i = 0; i < n && i < 8; ++i) info[i] = v[i];
+  return AK_OK;
+}
+
+extern "C" ak_status ak_plan_export(const ak_plan_t* p, int32_t* items, int64_t capacity,
+                                    int64_t* count, int32_t* kv_lens) {
+  if (!p || !count) return fail(AK_ERR_INVALID_ARG, "ak_plan_export: null argument");
+  const int64_t n = (int64_t)(p->small_items.size() + p->large_items.size());
+  *count = n;
+  if (kv_lens && p->R > 0) std::memcpy(kv_lens, p->kv_lens.data(), p->R * sizeof(int32_t));
+  if (n > capacity || (n > 0 && !items))
+    return fail(AK_ERR_INVALID_ARG, "ak_plan_export: item buffer too small");
+  int32_t* o = items;
+  for (const auto* v : {&p->small_items, &p->large_items})
+    for (const Item& it : *v) {
+      std::memcpy(o, &it, sizeof(Item));
+      o += 8;
+    }
+  return AK_OK;
+}
+
+extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* stream) {
+  if (!p || !slots) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: null argument");
+  if (p->host_only) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: plan was built host-only");
+  if (p->R == 0) return AK_OK;
+  std::vector<int64_t> off(p->R, 0);
+  int64_t acc = 0;
+  for (int r = 0; r < p->R; ++r) {
+    off[r] = acc;
+    acc += p->kv_lens[r];
+  }
+  if (acc == 0) return AK_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int64_t* d_off = nullptr;
+  hipError_t e = hipMalloc(&d_off, off.size() * sizeof(int64_t));
+  if (e != hipSuccess) return hip_fail(e, "ak_gather_slots: hipMalloc");
+  e = hipMemcpyAsync(d_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess)
+    e = launch_gather_slots(p->d_reqs, d_off, p->kv_indices, p->R, p->log2B, INT64_MAX >> 16,
+                            slots, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(d_off);
+  if (e != hipSuccess) return hip_fail(e, "ak_gather_slots");
+  return AK_OK;
+}
+
+extern "C" ak_status ak_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = on != 0;
+  return AK_OK;
+}
+
+extern "C" ak_status ak_profile_read(int64_t* launches, double* total_ms, int32_t n) {
+  std::vector<Profiler::Rec> recs;
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    recs.swap(g_prof.pending);
+  }
+  for (auto& r : recs) {
+    float ms = 0.f;
+    (void)hipEventSynchronize(r.b);
+    if (hipEventElapsedTime(&ms, r.a, r.b) == hipSuccess) {
+      g_prof.launches[r.kind] += 1;
+      g_prof.ms[r.kind] += ms;
+    }
+  }
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (auto& r : recs) {
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  for (int i = 0; i < n && i < kKinds; ++i) {
+    if (launches) launches[i] = g_prof.launches[i];
+    if (total_ms) total_ms[i] = g_prof.ms[i];
+  }
+  for (int i = 0; i < kKinds; ++i) {
+    g_prof.launches[i] = 0;
+    g_prof.ms[i] = 0.0;
+  }
+  return AK_OK;
+}
+
+extern "C" const char* ak_version(void) { return "ak 0.1 (gfx950)"; }

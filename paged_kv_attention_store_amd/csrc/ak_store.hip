@@ -1,0 +1,153 @@
+// store_kv: scatter this step's K/V rows into the paged cache by slot, and the
+// debug gather of the plan's slot arithmetic.
+//
+// "vLLM attention backend", "Write the KV first": the step's K/V are written
+// into the paged cache by slot_mapping before attention reads the cache.
+// Memory-bound: each thread moves 8 consecutive elements of one (token, head)
+// row per iteration with 16-byte (or wider) vector accesses; K and V are the
+// two planes of blockIdx.y.
+
+#include "ak_launch.h"
+
+namespace ak {
+
+namespace {
+
+template <int SRC>
+struct Load8;
+
+template <>
+struct Load8<AK_F32> {
+  __device__ static void run(const void* p, float (&x)[8]) {
+    const f32x4* v = reinterpret_cast<const f32x4*>(p);
+    f32x4 a = __builtin_nontemporal_load(v), b = __builtin_nontemporal_load(v + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = a[i];
+      x[4 + i] = b[i];
+    }
+  }
+};
+
+template <>
+struct Load8<AK_BF16> {
+  __device__ static void run(const void* p, float (&x)[8]) {
+    u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+      x[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+    }
+  }
+};
+
+template <int DST>
+struct Store8;
+
+template <>
+struct Store8<AK_F32> {
+  __device__ static void run(void* p, const float (&x)[8], float) {
+    f32x4* v = reinterpret_cast<f32x4*>(p);
+    v[0] = f32x4{x[0], x[1], x[2], x[3]};
+    v[1] = f32x4{x[4], x[5], x[6], x[7]};
+  }
+};
+
+template <>
+struct Store8<AK_BF16> {
+  __device__ static void run(void* p, const float (&x)[8], float) {
+    u32x4 w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(x[2 * i], x[2 * i + 1]);
+    *reinterpret_cast<u32x4*>(p) = w;
+  }
+};
+
+template <>
+struct Store8<AK_FP8_E4M3> {
+  __device__ static void run(void* p, const float (&x)[8], float scale) {
+    uint32_t c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = f32_to_e4m3(x[i] / scale);   // IEEE binary32 quotient
+    u32x2 w;
+    w[0] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    w[1] = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    *reinterpret_cast<u32x2*>(p) = w;
+  }
+};
+
+constexpr int elem_size(int dt) { return dt == AK_F32 ? 4 : (dt == AK_BF16 ? 2 : 1); }
+
+template <int SRC, int DST>
+__global__ __launch_bounds__(256) void store_kv_kernel(StoreArgs a) {
+  const int plane = blockIdx.y;
+  const int groups_per_head = a.D >> 3;
+  const int groups_per_tok = a.Hkv * groups_per_head;
+  const int64_t total = (int64_t)a.N * groups_per_tok;
+  const char* src = static_cast<const char*>(a.src[plane]);
+  char* dst = static_cast<char*>(a.dst[plane]);
+  const float scale = a.scale[plane];
+  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < total;
+       gi += (int64_t)gridDim.x * blockDim.x) {
+    const int tok = (int)(gi / groups_per_tok);
+    const int rem = (int)(gi - (int64_t)tok * groups_per_tok);
+    const int h = rem / groups_per_head;
+    const int d0 = (rem - h * groups_per_head) << 3;
+    const int64_t slot = a.slots[tok];
+    if (slot < 0 || slot >= a.num_slots) continue;
+    const int64_t page = slot / a.B;
+    const int64_t off = slot - page * a.B;
+    const char* sp = src + (tok * a.s_st[plane] + h * a.s_sh[plane] + d0) * elem_size(SRC);
+    char* dp = dst + (page * a.d_sp[plane] + off * a.d_sb[plane] + h * a.d_sh[plane] + d0) *
+                         elem_size(DST);
+    float x[8];
+    Load8<SRC>::run(sp, x);
+    Store8<DST>::run(dp, x, scale);
+  }
+}
+
+__global__ __launch_bounds__(256) void gather_slots_kernel(const Req* __restrict__ reqs,
+                                                           const int64_t* __restrict__ kv_off,
+                                                           const int32_t* __restrict__ kv_indices,
+                                                           int32_t log2B, int64_t num_pages,
+                                                           int64_t* __restrict__ slots) {
+  const Req rq = reqs[blockIdx.y];
+  const int64_t base = kv_off[blockIdx.y];
+  for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < rq.L; t += gridDim.x * blockDim.x) {
+    const int64_t page = kv_page(kv_indices, rq.page_off, t, log2B, num_pages);
+    slots[base + t] = (page << log2B) + (t & ((1 << log2B) - 1));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s) {
+  const int64_t total = (int64_t)a.N * a.Hkv * (a.D >> 3);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  dim3 grid((unsigned)blocks, 2);
+#define AK_STORE_CASE(S, D)                                                 \
+  if (src_dtype == S && dst_dtype == D) {                                   \
+    hipLaunchKernelGGL((store_kv_kernel<S, D>), grid, dim3(256), 0, s, a); \
+    return hipGetLastError();                                               \
+  }
+  AK_STORE_CASE(AK_F32, AK_F32)
+  AK_STORE_CASE(AK_F32, AK_BF16)
+  AK_STORE_CASE(AK_F32, AK_FP8_E4M3)
+  AK_STORE_CASE(AK_BF16, AK_BF16)
+  AK_STORE_CASE(AK_BF16, AK_FP8_E4M3)
+#undef AK_STORE_CASE
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int32_t* kv_indices,
+                               int32_t R, int32_t log2B, int64_t num_pages, int64_t* slots,
+                               hipStream_t s) {
+  if (R <= 0) return hipSuccess;
+  dim3 grid(64, (unsigned)R);
+  hipLaunchKernelGGL(gather_slots_kernel, grid, dim3(256), 0, s, reqs, kv_off, kv_indices, log2B,
+                     num_pages, slots);
+  return hipGetLastError();
+}
+
+}  // namespace ak

@@ -72,15 +72,42 @@ def _mix_np(x: np.ndarray) -> np.ndarray:
     return ((x >> 16) ^ x) & MASK32
 
 
-def table_index_np(seed: int, stream: str, idx: np.ndarray) -> np.ndarray:
+def _mix_np_inplace(x: np.ndarray) -> np.ndarray:
+    """_mix_np on an int64 array, in place (same values, fewer temporaries)."""
+    x &= MASK32
+    t = x >> 16
+    x ^= t
+    x *= MUL
+    x &= MASK32
+    t = x >> 16
+    x ^= t
+    x *= MUL
+    x &= MASK32
+    t = x >> 16
+    x ^= t
+    return x
+
+
+def table_index_np(seed: int, stream: str, idx: np.ndarray, chunk: int = 1 << 20) -> np.ndarray:
     """16-bit table indices for counters `idx` (any integer array, < 2^40)."""
     k1, k2 = stream_keys(seed, stream)
     idx = np.asarray(idx, dtype=np.int64)
-    lo = idx & MASK32
-    hi = idx >> 32
-    h = _mix_np(lo ^ k1)
-    h = _mix_np(h ^ _mix_np(hi ^ k2))
-    return (h & 0xFFFF).astype(np.int64)
+    shape = idx.shape
+    flat = idx.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.int64)
+    for s in range(0, len(flat), chunk):
+        c = flat[s:s + chunk]
+        hi = c >> 32
+        h = c & MASK32
+        h ^= k1
+        _mix_np_inplace(h)
+        hi ^= k2
+        _mix_np_inplace(hi)
+        h ^= hi
+        _mix_np_inplace(h)
+        h &= 0xFFFF
+        out[s:s + chunk] = h
+    return out.reshape(shape)
 
 
 def values_np(seed: int, stream: str, idx: np.ndarray, dtype: str) -> np.ndarray:

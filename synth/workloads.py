@@ -299,3 +299,12 @@ def device_inputs(wl: Workload, device, with_pool: bool = True) -> dict:
                 rng.fill_torch(c, wl.seed, f"{w}_pool")
                 out[f"{w}_cache"] = c
     return out
+
+
+def custom(seed: int, q_lens, kv_lens, page_size: int, num_qo_heads: int, num_kv_heads: int,
+           head_dim: int, q_dtype: str = "bf16", kv_dtype: str = "bf16", causal: bool = True,
+           windows=(-1,), spare_pages: int = 3, name: str = "custom") -> Workload:
+    """A workload with given per-request query and KV lengths (edge-case tests)."""
+    _, g_perm, _, _ = _streams(seed)
+    return _assemble(name, seed, q_lens, kv_lens, page_size, g_perm, num_qo_heads, num_kv_heads,
+                     head_dim, q_dtype, kv_dtype, causal, windows, spare_pages=spare_pages)

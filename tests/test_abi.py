@@ -1,0 +1,45 @@
+"""The C-ABI library loads and exports every symbol include/ak.h declares (no GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "ak.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ak_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("ak_store_kv", "ak_plan", "ak_run", "ak_plan_destroy", "ak_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import paged_kv_attention_store_amd as ak
+
+    lib = ctypes.CDLL(ak.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(ak.EXPORTED) == set(_declared())
+
+
+def test_version_and_error_text():
+    import paged_kv_attention_store_amd as ak
+
+    assert "gfx950" in ak.ak_version()
+    assert isinstance(ak.ak_last_error(), str)
+
+
+def test_binding_struct_layout_matches_header():
+    import paged_kv_attention_store_amd as ak
+
+    # ak_tensor: void* + 2*int32 + 4*int64 + 4*int64 + float (+ padding) = 88 bytes
+    assert ctypes.sizeof(ak.AkTensor) == 88
+    assert ctypes.sizeof(ak.AkPlanOpts) == 32

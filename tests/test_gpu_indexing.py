@@ -1,0 +1,30 @@
+"""The plan's KV indexing on the GPU, bit-exact against the oracle's slot
+arithmetic, and the exported work list of every workload."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_store_amd as ak
+from oracle import metadata as M
+from synth import workloads as W
+from tests.gpu_harness import plan_for, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_gather_slots_bit_exact(k):
+    say(f"[indexing] config {k}")
+    wl = W.config(k)
+    idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).cuda()
+    plan = plan_for(wl, {"kv_indices": idx}, wl.windows[0])
+    total = int(wl.kv_lens.sum())
+    slots = torch.full((total,), -7, dtype=torch.int64, device="cuda")
+    ak.ak_gather_slots(plan, slots)
+    got = slots.cpu().numpy()
+    exp = np.concatenate([M.request_slots(wl.kv_indptr, wl.kv_indices, wl.last_page_len,
+                                          wl.page_size, r) for r in range(wl.batch_size)])
+    assert np.array_equal(got, exp)
+    items, lens = ak.ak_plan_export(plan)
+    assert lens.tolist() == M.kv_lengths(wl.kv_indptr, wl.last_page_len, wl.page_size).tolist()

@@ -1,0 +1,181 @@
+"""Attention on the GPU against the fp64 CPU oracle, element by element on the
+same seeded inputs: the five workloads at reduced sizes (full comparison), at
+their full sizes (sampled requests / query rows, in the launch configuration
+the benchmark times), and edge cases."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_store_amd as ak
+from synth import rng as R
+from synth import workloads as W
+from tests.gpu_harness import check, plan_for, prepare, run, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _full(wl, windows=None, **plan_kw):
+    d = prepare(wl)
+    for window in (windows or wl.windows):
+        plan = plan_for(wl, d, window, **plan_kw)
+        say(f"[parity] {wl.name} {ak.ak_plan_info(plan)}")
+        out, lse = run(wl, d, plan)
+        check(wl, out, lse, window)
+
+
+# ------------------------------------------------ reduced-size workloads
+
+def test_tiny_decode_fp32():
+    _full(W.config(1))
+
+
+def test_decode_bf16_reduced():
+    _full(W.llama8b_decode(seed=2, R=8))
+
+
+def test_prefill_bf16_reduced():
+    _full(W.ragged_prefill(seed=3, R=4, n_range=(100, 300), p_range=(0, 600)))
+
+
+def test_mixed_bf16_reduced():
+    wl = W.mixed_chunk_decode(seed=4, R_dec=40, chunk=300, prefix=700, lmin=100, lmax=6000)
+    _full(wl, windows=(-1, 4096, 256))
+
+
+def test_mixed_bf16_reduced_shuffled():
+    wl = W.mixed_chunk_decode(seed=4, R_dec=40, chunk=300, prefix=700, lmin=100, lmax=6000,
+                              shuffle=True)
+    _full(wl, windows=(-1, 256))
+
+
+def test_long_decode_fp8_reduced():
+    _full(W.llama70b_long_decode(seed=5, R=2, L=20000))
+
+
+# ---------------------------------------------- full sizes, sampled checks
+
+def _sample_rows(wl, r, k=24):
+    n = int(wl.q_lens[r])
+    if n <= k:
+        return np.arange(n)
+    rng = np.random.default_rng(r)
+    pick = set([0, 1, n // 2, n - 2, n - 1]) | set(rng.choice(n, size=k, replace=False).tolist())
+    return np.asarray(sorted(pick))
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_full_size_sampled(k):
+    wl = W.config(k)
+    say(f"[parity-full] config {k}: R={wl.batch_size} tokens={wl.total_q} "
+        f"kv={int(wl.kv_lens.sum())}")
+    d = prepare(wl)
+    order = np.argsort(-wl.kv_lens)
+    rng = np.random.default_rng(k)
+    if k == 5:
+        reqs = [int(order[0]), int(order[-1])]
+    else:
+        reqs = sorted(set(order[:3].tolist()) | set(order[-2:].tolist()) |
+                      set(rng.choice(wl.batch_size, size=min(6, wl.batch_size), replace=False).tolist()))
+    for window in wl.windows:
+        plan = plan_for(wl, d, window)
+        say(f"  plan {ak.ak_plan_info(plan)}")
+        out, lse = run(wl, d, plan)
+        check(wl, out, lse, window, requests=reqs, rows_of=lambda r: _sample_rows(wl, r))
+
+
+# ------------------------------------------------------------- properties
+
+def test_plan_reuse_across_layers_and_determinism():
+    wl = W.llama8b_decode(seed=2, R=8)
+    d = prepare(wl)
+    plan = plan_for(wl, d, -1, min_chunk=64)
+    assert ak.ak_plan_info(plan)["split_units"] > 0
+    first = run(wl, d, plan)
+    again = run(wl, d, plan)
+    assert torch.equal(first[0], again[0]) and torch.equal(first[1], again[1])
+    for layer in range(3):   # fresh Q per "layer", same plan
+        q = torch.empty_like(d["q"])
+        R.fill_torch(q, 100 + layer, "q")
+        out, lse = run(wl, d, plan, q=q)
+        from tests.gpu_harness import compare
+        from oracle import workload_run as orun
+        qh = R.values_np(100 + layer, "q", np.arange(q.numel()), "bf16").reshape(q.shape)
+        ref_o, ref_l = orun.run(wl, q=qh.astype(np.float64))
+        eo = float(np.max(np.abs(out.float().cpu().numpy() - ref_o)))
+        el = float(np.max(np.abs(lse.cpu().numpy() - ref_l)))
+        say(f"  layer {layer}: max|dout|={eo:.3e} max|dlse|={el:.3e}")
+        assert eo <= 2e-2 and el <= 1e-3
+
+
+@pytest.mark.parametrize("min_chunk,max_splits", [(64, 0), (64, 2), (256, 3)])
+def test_forced_splits(min_chunk, max_splits):
+    wl = W.llama8b_decode(seed=7, R=6)
+    d = prepare(wl)
+    plan = plan_for(wl, d, -1, min_chunk=min_chunk, max_splits=max_splits, num_cus=512)
+    info = ak.ak_plan_info(plan)
+    assert info["split_units"] > 0
+    out, lse = run(wl, d, plan)
+    check(wl, out, lse, -1)
+
+
+# ------------------------------------------------------------- edge cases
+
+EDGE = [
+    # name, q_lens, kv_lens, B, hq, hkv, D, q_dtype, kv_dtype, causal, windows
+    ("one_key", [1, 1, 1], [1, 2, 17], 16, 8, 2, 128, "bf16", "bf16", True, (-1, 0)),
+    ("zero_query_rows", [0, 3, 0, 1], [5, 40, 9, 70], 16, 8, 2, 128, "bf16", "bf16", True, (-1, 4)),
+    ("page_size_1", [1, 5, 1], [300, 77, 1], 1, 32, 8, 128, "bf16", "bf16", True, (-1, 31)),
+    ("page_size_256", [1, 2, 130], [1000, 513, 700], 256, 32, 8, 128, "bf16", "bf16", True, (-1, 100)),
+    ("mha_g1", [1, 20, 1], [90, 200, 400], 16, 8, 8, 128, "bf16", "bf16", True, (-1,)),
+    ("gqa_g16", [1, 1, 9], [700, 65, 300], 16, 32, 2, 128, "bf16", "bf16", True, (-1, 50)),
+    ("head_dim_64", [1, 37, 1], [333, 260, 64], 16, 16, 4, 64, "bf16", "bf16", True, (-1, 20)),
+    ("non_causal", [64, 200, 1], [64, 511, 90], 16, 8, 2, 128, "bf16", "bf16", False, (-1,)),
+    ("fp8_prefill", [1, 150, 2], [3000, 900, 65], 64, 16, 2, 128, "bf16", "fp8", True, (-1, 300)),
+    ("fp32_prefill", [1, 70, 3], [40, 100, 200], 16, 8, 2, 64, "f32", "f32", True, (-1, 10)),
+    ("fp32_d128", [2, 1], [33, 129], 4, 4, 1, 128, "f32", "f32", True, (-1,)),
+    ("multi_row_small", [2, 4, 3], [2000, 1500, 999], 16, 8, 2, 128, "bf16", "bf16", True, (-1, 700)),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
+def test_edge_cases(case):
+    name, ql, kl, B, hq, hkv, D, qd, kd, causal, windows = case
+    wl = W.custom(seed=len(name) * 31 + sum(kl), q_lens=ql, kv_lens=kl, page_size=B,
+                  num_qo_heads=hq, num_kv_heads=hkv, head_dim=D, q_dtype=qd, kv_dtype=kd,
+                  causal=causal, windows=windows, name=name)
+    say(f"[edge] {name}")
+    d = prepare(wl)
+    for window in windows:
+        for kw in ({}, {"min_chunk": 64, "num_cus": 1024}):
+            plan = plan_for(wl, d, window, **kw)
+            out, lse = run(wl, d, plan)
+            check(wl, out, lse, window)
+
+
+def test_empty_batch_launches_nothing():
+    q = torch.empty(0, 8, 128, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(2, 16, 2, 128, dtype=torch.bfloat16, device="cuda")
+    idx = torch.zeros(0, dtype=torch.int32, device="cuda")
+    plan = ak.ak_plan([0], [0], idx, [], 8, 2, 128, 16)
+    out, _ = ak.ak_run(plan, q, kc, kc)
+    assert out.shape == q.shape
+
+
+def test_run_rejects_mismatched_geometry():
+    wl = W.custom(seed=9, q_lens=[1, 1], kv_lens=[20, 30], page_size=16, num_qo_heads=8,
+                  num_kv_heads=2, head_dim=128)
+    d = prepare(wl)
+    plan = plan_for(wl, d, -1)
+    q16 = torch.zeros(2, 16, 128, dtype=torch.bfloat16, device="cuda")   # more heads than planned
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_run(plan, q16, d["k_cache"], d["v_cache"])
+    assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_run(plan, d["q"].float(), d["k_cache"], d["v_cache"])
+    assert e.value.status == ak.AK_ERR_UNSUPPORTED
+    kc8 = d["k_cache"].view(-1)[: d["k_cache"].numel() // 2].view(
+        d["k_cache"].shape[0], 8, 2, 128)                                  # wrong page size
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_run(plan, d["q"], kc8, kc8)
+    assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH

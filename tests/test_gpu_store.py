@@ -1,0 +1,111 @@
+"""store_kv on the GPU, bit-exact against the oracle's store (all five workloads,
+both readings of the tiny workload's store, every dtype conversion)."""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_attention_store_amd as ak
+from oracle import attention as A
+from oracle import codecs as C
+from oracle import workload_run as orun
+from synth import workloads as W
+from tests.gpu_harness import prepare, say
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    t = t.cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def _cache_rows(cache, slots):
+    P, B, H, D = cache.shape
+    flat = cache.view(P * B, H, D)
+    return _bits(flat[torch.from_numpy(np.asarray(slots)).to(cache.device)])
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
+def test_store_new_tokens_bit_exact(k):
+    say(f"[store] config {k}")
+    wl = W.config(k)
+    d = prepare(wl)
+    torch.cuda.synchronize()
+    kc, vc = orun.caches_after_store(wl)
+    slots = wl.slot_mapping
+    for w, cache, oc in (("k", d["k_cache"], kc), ("v", d["v_cache"], vc)):
+        got = _cache_rows(cache, slots)
+        exp = oc.codes_at(slots)
+        assert np.array_equal(got.view(np.uint8), exp.view(np.uint8)), f"{w} new rows differ"
+        # untouched pool rows keep their generated (and, for fp8, quantised) codes
+        rng = np.random.default_rng(k)
+        other = rng.choice(wl.pool_slots, size=min(2048, wl.pool_slots), replace=False)
+        other = np.setdiff1d(other, slots)
+        assert np.array_equal(_cache_rows(cache, other).view(np.uint8),
+                              oc.codes_at(other).view(np.uint8)), f"{w} pool rows differ"
+
+
+def test_tiny_store_reading_b_free_slots():
+    wl = W.config(1)
+    d = prepare(wl, store_new=False)
+    free = wl.extra["free_slots"]
+    ak.ak_store_kv(d["k_new"], d["v_new"], torch.from_numpy(free).cuda(), d["k_cache"],
+                   d["v_cache"])
+    torch.cuda.synchronize()
+    kc, vc = orun.caches_after_store(wl, slot_mapping=free)
+    # the whole pool, bit for bit
+    every = np.arange(wl.pool_slots)
+    assert np.array_equal(_cache_rows(d["k_cache"], every), kc.codes_at(every))
+    assert np.array_equal(_cache_rows(d["v_cache"], every), vc.codes_at(every))
+
+
+@pytest.mark.parametrize("src,dst", [("f32", "f32"), ("f32", "bf16"), ("f32", "fp8"),
+                                     ("bf16", "bf16"), ("bf16", "fp8")])
+def test_conversions_and_padding(src, dst):
+    rng = np.random.default_rng(5)
+    N, H, D, P, B = 300, 2, 64, 40, 16
+    vals = (rng.standard_normal((N, H, D)) * rng.choice([1e-3, 1.0, 30.0, 300.0], size=(N, 1, 1)))
+    vals = vals.astype(np.float32)
+    # exact bf16 ties and e4m3 ties in the first rows
+    vals[0, 0, :16] = ((np.arange(16, dtype=np.uint32) << 16) + 0x3F808000).view(np.float32)
+    vals[1, 0, :8] = np.array([1.0625, 1.1875, 0.0048828125 * 1.5, 448.0, 464.0, -500.0,
+                               2 ** -10, -(2 ** -10) * 3], dtype=np.float32)
+    if src == "bf16":
+        vals = C.bf16_decode(C.bf16_encode(vals)).astype(np.float32)
+    scale = 0.25 if dst == "fp8" else 1.0
+    slots = rng.permutation(P * B)[:N].astype(np.int64)
+    slots[::7] = -1                                    # padding rows are skipped
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    k = torch.from_numpy(vals).to(tdt[src]).cuda() if src == "f32" else \
+        torch.from_numpy(C.bf16_encode(vals).view(np.int16)).view(torch.bfloat16).cuda()
+    v = -k
+    kc = torch.zeros(P, B, H, D, dtype=tdt[dst], device="cuda")
+    vc = torch.zeros_like(kc)
+    ak.ak_store_kv(k, v, torch.from_numpy(slots).cuda(), kc, vc, scale, scale)
+    torch.cuda.synchronize()
+    zero = np.zeros((P, B, H, D), dtype=np.float32)
+    for sign, cache in ((1, kc), (-1, vc)):
+        oc = A.Cache(A.encode(zero, dst, scale), dst, scale)
+        A.store_kv(oc, sign * vals, slots)
+        got = _bits(cache).reshape(-1)
+        assert np.array_equal(got.view(np.uint8), oc.codes.reshape(-1).view(np.uint8))
+
+
+def test_store_rejects_bad_arguments():
+    k = torch.zeros(4, 2, 64, dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros(2, 16, 2, 64, dtype=torch.bfloat16, device="cuda")
+    s32 = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_store_kv(k, k, s32, kc, kc.clone())
+    assert e.value.status == ak.AK_ERR_UNSUPPORTED
+    kf = torch.zeros(2, 16, 2, 64, dtype=torch.float32, device="cuda")
+    s64 = torch.zeros(4, dtype=torch.int64, device="cuda")
+    with pytest.raises(ak.AkError) as e:           # bf16 -> f32 widening is not a store
+        ak.ak_store_kv(k, k, s64, kf, kf.clone())
+    assert e.value.status == ak.AK_ERR_UNSUPPORTED
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_store_kv(k, k, s64[:3], kc, kc.clone())
+    assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH
