@@ -1,30 +1,30 @@
 """Benchmark of the paged-KV attention hot path on one MI355X.
 
-A step is one decode step of a Llama-3-8B-shaped model over a 64-request batch
-(KV lengths uniform in [512, 8192], 32 q / 8 kv heads, head_dim 128, bf16,
+Headline step: one decode step of a Llama-3-8B-shaped model over a 64-request
+batch (KV lengths uniform in [512, 8192], 32 q / 8 kv heads, head_dim 128, bf16,
 page size 16, pages a random permutation of the pool): one ak_plan for the
 batch, then for each of the 32 layers ak_store_kv of the 64 new K/V rows into
 that layer's own cache followed by ak_run (split-KV decode + LSE merge).  All
 inputs are resident in HBM before the timed region.
 
 `value` = algorithmic HBM bytes of the step / step time (GB/s).  Algorithmic
-bytes per layer = visible KV (K and V) + Q + out + lse + page ids read, plus
-the store's read and write.  The roofline object reports the decode attention
-kernel alone: its algorithmic bytes per launch over its average duration from
-HIP events recorded around every launch on the launch stream.
+bytes per layer = visible KV rows (K and V) + Q + out + lse + page ids read,
+plus the store's reads and writes.  The roofline object reports the decode
+attention kernel alone: its algorithmic bytes per launch over its average
+duration from HIP events recorded around every launch on the launch stream.
 
-A second measurement (reported under "prefill") runs the ragged extend batch
-(8 requests, 128..2048 new tokens over a 0..4096-token prefix, page size 1) and
-reports the large-tile kernel's TFLOP/s against the bf16 dense MFMA peak.
+Further workloads (--also) are reported under their names: the ragged extend
+batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
+the mixed chunked-prefill + decode step with full and sliding-window layers
+("mixed"), and the fp8 long-context decode ("longfp8").
 
-The CPU baseline times the float64 oracle on a sample of the same decode batch.
+The CPU baseline times the float64 oracle on a sample of the decode batch.
 """
 
 from __future__ import annotations
 
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -37,61 +37,84 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)"
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
+EB = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def decode_bytes(wl, window=-1):
-    """Algorithmic HBM bytes of one ak_run over the batch."""
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}
-    kv_tok = 0
-    for L, n in zip(wl.kv_lens, wl.q_lens):
-        if n == 0:
+# ------------------------------------------------------- algorithmic work
+
+def decode_bytes(wl, window=-1, small_only=False):
+    """Algorithmic HBM bytes of one ak_run: visible KV rows (K and V), Q, out,
+    lse and page ids.  `small_only` counts only requests whose rows per KV head
+    (queries x group) fit a decode-shaped tile (<= 16)."""
+    kv_tok = q_tok = pages = 0
+    for r, (L, n) in enumerate(zip(wl.kv_lens, wl.q_lens)):
+        L, n = int(L), int(n)
+        if n == 0 or (small_only and n * wl.group > 16):
             continue
-        vis = int(L) if window < 0 else min(int(L), window + int(n))
-        kv_tok += vis
-    kv = kv_tok * wl.num_kv_heads * wl.head_dim * 2 * eb[wl.kv_dtype]
-    qo = wl.total_q * wl.num_qo_heads * wl.head_dim * eb[wl.q_dtype] * 2
-    lse = wl.total_q * wl.num_qo_heads * 4
-    idx = int(wl.kv_indptr[-1]) * 4
-    return kv + qo + lse + idx
+        kv_tok += L if window < 0 else min(L, window + n)
+        q_tok += n
+        pages += int(wl.kv_indptr[r + 1] - wl.kv_indptr[r])
+    kv = kv_tok * wl.num_kv_heads * wl.head_dim * 2 * EB[wl.kv_dtype]
+    qo = q_tok * wl.num_qo_heads * wl.head_dim * EB[wl.q_dtype] * 2
+    return kv + qo + q_tok * wl.num_qo_heads * 4 + pages * 4
 
 
 def store_bytes(wl):
-    eb = {"f32": 4, "bf16": 2, "fp8": 1}
     n = len(wl.slot_mapping)
-    per = wl.num_kv_heads * wl.head_dim * 2
-    return n * per * (eb[wl.q_dtype] + eb[wl.kv_dtype]) + 8 * n
+    return n * wl.num_kv_heads * wl.head_dim * 2 * (EB[wl.q_dtype] + EB[wl.kv_dtype]) + 8 * n
 
 
-def prefill_flops(wl, window=-1):
-    """4 * D * Hq * (visible (query, key) pairs), causal/window aware."""
+def prefill_flops(wl, window=-1, large_only=False):
+    """4 * D * Hq * (visible (query, key) pairs), causal/window aware.
+    `large_only` counts only requests with more than 16 rows per KV head."""
     pairs = 0
     for L, n in zip(wl.kv_lens, wl.q_lens):
         L, n = int(L), int(n)
-        for j in range(n):
-            p = L - n + j
-            lo = 0 if window < 0 else max(0, p - window)
-            pairs += p - lo + 1
+        if n == 0 or (large_only and n * wl.group <= 16):
+            continue
+        p = np.arange(L - n, L)
+        lo = np.zeros_like(p) if window < 0 else np.maximum(0, p - window)
+        pairs += int((p - lo + 1).sum())
     return 4.0 * wl.head_dim * wl.num_qo_heads * pairs
 
 
+# ------------------------------------------------------------- device side
+
 def make_layers(wl, n_layers, dev):
+    """Per-layer caches (each its own pool), Q, new K/V and outputs on the device.
+    FP8 pools are quantised from generated bf16 values by the library's store."""
     import torch
 
+    import paged_kv_attention_store_amd as ak
     from synth import rng as R
 
     qd = torch.bfloat16 if wl.q_dtype == "bf16" else torch.float32
     shape = (wl.num_pages, wl.page_size, wl.num_kv_heads, wl.head_dim)
+    flat = (wl.num_pages * wl.page_size, wl.num_kv_heads, wl.head_dim)
     layers = []
     for l in range(n_layers):
         s = wl.seed * 1000 + l
-        kc = torch.empty(shape, dtype=qd, device=dev)
-        vc = torch.empty(shape, dtype=qd, device=dev)
-        R.fill_torch(kc, s, "k_pool")
-        R.fill_torch(vc, s, "v_pool")
+        if wl.kv_dtype == "fp8":
+            kc = torch.empty(shape, dtype=torch.uint8, device=dev)
+            vc = torch.empty(shape, dtype=torch.uint8, device=dev)
+            ksrc = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            vsrc = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            R.fill_torch(ksrc, s, "k_pool")
+            R.fill_torch(vsrc, s, "v_pool")
+            all_slots = torch.arange(flat[0], dtype=torch.int64, device=dev)
+            ak.ak_store_kv(ksrc.view(flat), vsrc.view(flat), all_slots, kc, vc, wl.kv_scale,
+                           wl.kv_scale)
+            torch.cuda.synchronize()
+            del ksrc, vsrc, all_slots
+        else:
+            kc = torch.empty(shape, dtype=qd, device=dev)
+            vc = torch.empty(shape, dtype=qd, device=dev)
+            R.fill_torch(kc, s, "k_pool")
+            R.fill_torch(vc, s, "v_pool")
         q = torch.empty(wl.total_q, wl.num_qo_heads, wl.head_dim, dtype=qd, device=dev)
         R.fill_torch(q, s, "q")
         kn = torch.empty(len(wl.slot_mapping), wl.num_kv_heads, wl.head_dim, dtype=qd, device=dev)
@@ -104,87 +127,78 @@ def make_layers(wl, n_layers, dev):
     return layers
 
 
-def run_steps(ak, wl, layers, idx, slots, steps, window=-1):
-    import torch
-
+def run_steps(ak, wl, layers, idx, slots, steps):
+    """`steps` steps: one plan per window setting, then every layer stores its new
+    K/V and runs with the plan of its window (layers alternate windows)."""
     plan_s = 0.0
+    plans = None
     for _ in range(steps):
         t = time.perf_counter()
-        plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, wl.num_qo_heads,
-                          wl.num_kv_heads, wl.head_dim, wl.page_size, causal=wl.causal,
-                          window=window)
+        plans = [ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, wl.num_qo_heads,
+                            wl.num_kv_heads, wl.head_dim, wl.page_size, causal=wl.causal,
+                            window=w) for w in wl.windows]
         plan_s += time.perf_counter() - t
-        for L in layers:
-            ak.ak_store_kv(L["kn"], L["vn"], slots, L["kc"], L["vc"])
-            ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
-    return plan_s, plan
+        for i, L in enumerate(layers):
+            ak.ak_store_kv(L["kn"], L["vn"], slots, L["kc"], L["vc"], wl.kv_scale, wl.kv_scale)
+            ak.ak_run(plans[i % len(plans)], L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"],
+                      k_scale=wl.kv_scale, v_scale=wl.kv_scale)
+    return plan_s, plans
 
 
-def bench_decode(args, ak, torch, dev):
-    from synth import workloads as W
-
-    wl = W.config(2)
-    log(f"[bench] decode workload {wl.name}: R={wl.batch_size} KV tokens={int(wl.kv_lens.sum())} "
-        f"layers={args.layers}")
-    layers = make_layers(wl, args.layers, dev)
+def measure(ak, torch, dev, wl, n_layers, steps, warmup):
+    """Time `steps` steps of the workload; per-kernel HIP-event times included."""
+    log(f"[bench] {wl.name}: R={wl.batch_size} new tokens={wl.total_q} "
+        f"KV tokens={int(wl.kv_lens.sum())} layers={n_layers} windows={wl.windows}")
+    layers = make_layers(wl, n_layers, dev)
     idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
     slots = torch.from_numpy(wl.slot_mapping).to(dev)
     torch.cuda.synchronize()
-    run_steps(ak, wl, layers, idx, slots, args.warmup)
+    run_steps(ak, wl, layers, idx, slots, warmup)
     torch.cuda.synchronize()
     ak.ak_profile_read()                      # reset counters
     ak.ak_profile_enable(True)
     t0 = time.perf_counter()
-    plan_s, plan = run_steps(ak, wl, layers, idx, slots, args.steps)
+    plan_s, plans = run_steps(ak, wl, layers, idx, slots, steps)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ak.ak_profile_enable(False)
     prof = ak.ak_profile_read()
-    info = ak.ak_plan_info(plan)
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    b_layer = decode_bytes(wl) + store_bytes(wl)
-    step_bytes = args.layers * b_layer
-    gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    n_att, ms_att = prof["attn_small"]
-    att_avg_ms = ms_att / max(n_att, 1)
-    att_gbs = decode_bytes(wl) / (att_avg_ms * 1e-3) / 1e9
-    log(f"[bench] decode: {ms_step:.3f} ms/step, {gbs:.1f} GB/s step-level; attn_small avg "
-        f"{att_avg_ms * 1e3:.1f} us -> {att_gbs:.1f} GB/s; plan {plan_s / args.steps * 1e6:.1f} us; "
-        f"profile {prof}; plan info {info}")
-    return dict(wl=wl, ms_step=ms_step, gbs=gbs, att_avg_ms=att_avg_ms, att_gbs=att_gbs,
-                prof=prof, info=info, plan_us=plan_s / args.steps * 1e6, b_layer=b_layer)
-
-
-def bench_prefill(args, ak, torch, dev):
-    from synth import workloads as W
-
-    wl = W.config(3)
-    flops = prefill_flops(wl)
-    log(f"[bench] prefill workload {wl.name}: new tokens={wl.total_q} flops={flops / 1e9:.1f} G")
-    layers = make_layers(wl, 2, dev)
-    idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
-    slots = torch.from_numpy(wl.slot_mapping).to(dev)
-    run_steps(ak, wl, layers, idx, slots, 2)
-    torch.cuda.synchronize()
-    ak.ak_profile_read()
-    ak.ak_profile_enable(True)
-    steps = max(2, args.steps // 2)
-    t0 = time.perf_counter()
-    run_steps(ak, wl, layers, idx, slots, steps)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ak.ak_profile_enable(False)
-    prof = ak.ak_profile_read()
+    ms_step = (t1 - t0) * 1e3 / steps
+    wins = [wl.windows[i % len(wl.windows)] for i in range(n_layers)]
+    dec_bytes = sum(decode_bytes(wl, w, small_only=True) for w in wins)
+    flops = sum(prefill_flops(wl, w, large_only=True) for w in wins)
+    step_bytes = sum(decode_bytes(wl, w) for w in wins) + n_layers * store_bytes(wl)
+    res = dict(wl=wl, ms_step=ms_step, gbs=step_bytes / (ms_step * 1e-3) / 1e9, prof=prof,
+               info=ak.ak_plan_info(plans[0]), plan_us=plan_s / steps * 1e6,
+               step_bytes=step_bytes, layers=n_layers)
+    n, ms = prof["attn_small"]
+    if n and dec_bytes:
+        res["small_avg_ms"] = ms / n
+        res["small_gbs"] = dec_bytes * steps / (ms * 1e-3) / 1e9
     n, ms = prof["attn_large"]
-    avg = ms / max(n, 1)
-    tflops = flops / (avg * 1e-3) / 1e12
-    ns, mss = prof["store_kv"]
-    st_avg = mss / max(ns, 1)
-    st_gbs = store_bytes(wl) / (st_avg * 1e-3) / 1e9
-    log(f"[bench] prefill: attn_large avg {avg * 1e3:.1f} us -> {tflops:.1f} TFLOP/s; "
-        f"store_kv avg {st_avg * 1e3:.1f} us -> {st_gbs:.1f} GB/s; step {(t1 - t0) * 1e3 / steps / 2:.3f} ms/layer")
-    return dict(tflops=tflops, avg_ms=avg, flops=flops, store_gbs=st_gbs, store_us=st_avg * 1e3)
+    if n and flops:
+        res["large_avg_ms"] = ms / n
+        res["large_tflops"] = flops * steps / (ms * 1e-3) / 1e12
+    n, ms = prof["store_kv"]
+    if n:
+        res["store_avg_us"] = ms / n * 1e3
+        res["store_gbs"] = store_bytes(wl) / (ms / n * 1e-3) / 1e9
+    n, ms = prof["merge"]
+    if n:
+        res["merge_avg_us"] = ms / n * 1e3
+    msg = (f"[bench] {wl.name}: {ms_step:.3f} ms/step, step-level {res['gbs']:.1f} GB/s; "
+           f"plan {res['plan_us']:.1f} us; ")
+    if "small_gbs" in res:
+        msg += f"attn_small {res['small_avg_ms'] * 1e3:.1f} us -> {res['small_gbs']:.1f} GB/s; "
+    if "large_tflops" in res:
+        msg += f"attn_large {res['large_avg_ms'] * 1e3:.1f} us -> {res['large_tflops']:.1f} TFLOP/s; "
+    log(msg + f"profile {prof}; plan {res['info']}")
+    del layers
+    torch.cuda.empty_cache()
+    return res
 
+
+# ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(wl, budget_s=12.0, n_req=16):
     """The float64 oracle as it stands, on a sample of the decode batch."""
@@ -197,12 +211,11 @@ def cpu_baseline(wl, budget_s=12.0, n_req=16):
     kc, vc = orun.caches_after_store(wl)
     sl = np.concatenate([M.request_slots(wl.kv_indptr, wl.kv_indices, wl.last_page_len,
                                          wl.page_size, r) for r in reqs])
-    kc.materialize(sl)
+    kc.materialize(sl)          # input generation is not timed
     vc.materialize(sl)
     q = orun.decoded_q(wl)
-    sub = dict(kv_lens=wl.kv_lens[reqs])
-    kv_bytes = int(sub["kv_lens"].sum()) * wl.num_kv_heads * wl.head_dim * 2 * 2
-    qo = n_req * wl.num_qo_heads * wl.head_dim * 2 * 2
+    kv_tok = int(wl.kv_lens[reqs].sum())
+    work = kv_tok * wl.num_kv_heads * wl.head_dim * 2 * 2 + n_req * wl.num_qo_heads * wl.head_dim * 4
     passes, t = 0, 0.0
     while t < budget_s:
         t0 = time.perf_counter()
@@ -210,11 +223,21 @@ def cpu_baseline(wl, budget_s=12.0, n_req=16):
         t += time.perf_counter() - t0
         passes += 1
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    gbs = (kv_bytes + qo) * passes / t / 1e9
-    return {"value": round(gbs, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_req} of {wl.batch_size} decode requests ({int(sub['kv_lens'].sum())} KV "
-                      f"tokens), one layer, {passes} passes in {t:.1f} s; host cores available "
-                      f"{len(os.sched_getaffinity(0))}"}
+    return {"value": round(work * passes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n_req} of {wl.batch_size} decode requests ({kv_tok} KV tokens), one layer, "
+                      f"{passes} passes in {t:.1f} s (same algorithmic-byte count as the GPU "
+                      f"metric); host cores available {len(os.sched_getaffinity(0))}"}
+
+
+# -------------------------------------------------------------------- main
+
+WORKLOADS = {
+    # name: (factory, layers with distinct caches)
+    "prefill": (lambda W: W.config(3), 2),
+    "mixed": (lambda W: W.config(4), 4),
+    "longfp8": (lambda W: W.config(5), 4),
+}
 
 
 def main():
@@ -222,8 +245,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--layers", type=int, default=32)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
+    ap.add_argument("--also", default="prefill",
+                    help="comma list of further workloads: prefill,mixed,longfp8 ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -234,10 +258,14 @@ def main():
     import torch
 
     import paged_kv_attention_store_amd as ak
+    from synth import workloads as W
 
     dev = torch.device("cuda:0")
-    dec = bench_decode(args, ak, torch, dev)
-    pre = None if args.no_prefill else bench_prefill(args, ak, torch, dev)
+    dec = measure(ak, torch, dev, W.config(2), args.layers, args.steps, args.warmup)
+    extra = {}
+    for name in [x for x in args.also.split(",") if x]:
+        fac, nl = WORKLOADS[name]
+        extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps // 2), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
     wl = dec["wl"]
     line = {
@@ -259,36 +287,40 @@ def main():
                         f"step = 1 plan + {args.layers} layers x (store_kv of 64 tokens + run)",
             "layers": args.layers,
             "kv_tokens": int(wl.kv_lens.sum()),
-            "bytes_per_layer": dec["b_layer"],
+            "bytes_per_step": dec["step_bytes"],
             "plan_us": round(dec["plan_us"], 1),
             "plan": dec["info"],
         },
         "roofline": {
             "bound": "hbm",
             "kernel": "attn_small (decode, split-KV)",
-            "achieved": round(dec["att_gbs"], 1),
+            "achieved": round(dec["small_gbs"], 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(dec["att_gbs"] / HBM_PEAK_GBS, 4),
-            "avg_launch_us": round(dec["att_avg_ms"] * 1e3, 2),
+            "frac": round(dec["small_gbs"] / HBM_PEAK_GBS, 4),
+            "avg_launch_us": round(dec["small_avg_ms"] * 1e3, 2),
             "traffic": None,
         },
         "cpu_baseline": cpu,
     }
-    if pre is not None:
-        line["prefill"] = {
-            "workload": "ragged extend: 8 requests, 128..2048 new tokens over 0..4096 prefix, "
-                        "32/8 heads, head_dim 128, bf16, page size 1",
-            "kernel": "attn_large",
-            "achieved": round(pre["tflops"], 2),
-            "peak": BF16_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(pre["tflops"] / BF16_PEAK_TFLOPS, 4),
-            "avg_launch_us": round(pre["avg_ms"] * 1e3, 2),
-            "gflop_per_launch": round(pre["flops"] / 1e9, 2),
-            "store_kv_GBs": round(pre["store_gbs"], 1),
-            "store_kv_us": round(pre["store_us"], 2),
-        }
+    for name, r in extra.items():
+        e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
+             "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1)}
+        if "small_gbs" in r:
+            e["decode"] = {"kernel": "attn_small", "achieved": round(r["small_gbs"], 1),
+                           "unit": "GB/s", "peak": HBM_PEAK_GBS,
+                           "frac": round(r["small_gbs"] / HBM_PEAK_GBS, 4),
+                           "avg_launch_us": round(r["small_avg_ms"] * 1e3, 2)}
+        if "large_tflops" in r:
+            e["prefill"] = {"kernel": "attn_large", "achieved": round(r["large_tflops"], 2),
+                            "unit": "TFLOP/s", "peak": BF16_PEAK_TFLOPS,
+                            "frac": round(r["large_tflops"] / BF16_PEAK_TFLOPS, 4),
+                            "avg_launch_us": round(r["large_avg_ms"] * 1e3, 2)}
+        if "store_gbs" in r:
+            e["store_kv"] = {"GBs": round(r["store_gbs"], 1), "avg_us": round(r["store_avg_us"], 2)}
+        if "merge_avg_us" in r:
+            e["merge_avg_us"] = round(r["merge_avg_us"], 2)
+        line[name] = e
     print(json.dumps(line), flush=True)
 
 

@@ -69,8 +69,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int k = 32; k >= 1; k >>= 1) mb = fmaxf(mb, shfl_xor_f(mb, k));
       const float m_new = fmaxf(m, mb);           // finite: key tb is visible
-      const float alpha = exp2f(m - m_new);
-      const float p = exp2f(s - m_new);
+      const float alpha = fast_exp2(m - m_new);
+      const float p = fast_exp2(s - m_new);
       float ps = p;
 #pragma unroll
       for (int k = 32; k >= 1; k >>= 1) ps += shfl_xor_f(ps, k);

@@ -8,15 +8,21 @@
 // head-group fusion figure of "Why metadata is built once per step".
 //
 // gfx950 mapping.  One workgroup of 4 waves per 128-row tile, wave w owning rows
-// 32w .. 32w+31.  The KV range is walked in 64-token blocks:
-//   * the block's K rows are gathered through the page table into LDS (16-byte
-//     chunks, XOR-swizzled by token so MFMA operand reads are conflict-free);
-//     V rows are gathered and written transposed (d-major, 4-token groups
-//     XOR-swizzled by d) so PV operands are two 8-byte reads;
-//   * S^T (64 tokens x 32 rows) = K Q^T with 32x32x16 bf16 MFMA, Q held in
-//     registers for the whole tile;
-//   * online softmax per row in base 2: a row lives in lanes n and n+32, so the
-//     block max needs one xor-shuffle;
+// 32w .. 32w+31; two workgroups share a CU (<= 256 registers per lane, 66 KB of
+// LDS each).  The KV range is walked in 64-token blocks with a software pipeline:
+//   * block i+1's K and V rows are loaded into registers while block i is
+//     computed from LDS, then written into the other LDS buffer (one barrier per
+//     block); the page ids of block i+2 are fetched one iteration earlier still;
+//   * K is staged as 16-byte chunks XOR-swizzled by token (conflict-free MFMA
+//     operand reads); V is staged transposed (d-major, 4-token groups swizzled
+//     by d) so a PV operand is two 8-byte reads;
+//   * S^T (64 tokens x 32 rows) = K Q^T with 32x32x16 bf16 MFMA, Q in registers;
+//   * softmax in base 2 with the scale folded into one FMA per score; a row lives
+//     in lanes n and n+32 (one xor-shuffle for its block max); masks are applied
+//     only on blocks that cross a row's causal or window bound;
+//   * the running max is raised only when a block exceeds it by more than 2^8
+//     (the normalisation is exact for any reference value; this only skips
+//     rescaling O, and probabilities stay below 2^8);
 //   * O^T (D x 32 rows) += V^T P^T, P taken from the S^T registers as produced.
 // FP8 caches are widened to bf16 while staging (exact).
 
@@ -26,8 +32,8 @@ namespace ak {
 
 namespace {
 
-constexpr int kKB = 64;       // tokens per KV block
-constexpr int kRows = 128;    // rows per tile
+constexpr int kKB = 64;          // tokens per KV block
+constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
 
 template <int D>
 __device__ __forceinline__ int k_pos(int t, int c) {
@@ -41,18 +47,23 @@ __device__ __forceinline__ int vt_pos(int d, int tg) {
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void attn_large_kernel(AttnArgs a) {
-  constexpr int NS = D / 16;      // S^T k-steps (16 d each)
-  constexpr int NDT = D / 32;     // O^T d-tiles (32 d each)
-  constexpr int CPR = D / 8;      // 16-byte bf16 chunks per row
-  __shared__ __align__(16) __bf16 ks[kKB * D];
-  __shared__ __align__(16) __bf16 vt[D * kKB];
-  __shared__ int64_t s_koff[kKB], s_voff[kKB];
+__global__ __launch_bounds__(256, 2) void attn_large_kernel(AttnArgs a) {
+  constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
+  constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
+  constexpr int CPR = D / 8;                  // 16-byte bf16 chunks per row
+  constexpr int SCPR = FP8 ? CPR / 2 : CPR;   // 16-byte source chunks per row
+  constexpr int KLD = kKB * SCPR / 256;       // K source chunks per thread per block
+  constexpr int VPAIRS = (kKB / 4) * CPR;     // (4-token group, 8-column chunk) pairs
+  static_assert(KLD >= 1 && VPAIRS <= 256, "tile shape");
+  __shared__ __align__(16) __bf16 ks[2][kKB * D];
+  __shared__ __align__(16) __bf16 vt[2][D * kKB];
+  __shared__ int64_t s_koff[2][kKB], s_voff[2][kKB];
 
   const Item it = a.items[blockIdx.x];
   const Req rq = a.reqs[it.r];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int n32 = lane & 31;
   const int hf = lane >> 5;
   const int G = a.G;
@@ -69,6 +80,14 @@ __global__ __launch_bounds__(256) void attn_large_kernel(AttnArgs a) {
   if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
   if (a.causal) row_hi = min(row_hi, qpos + 1);
   if (!rvalid) row_lo = row_hi = 0;
+  // blocks entirely inside [wave_lo_max, wave_hi_min) need no mask
+  int wave_lo_max = row_lo, wave_hi_min = row_hi;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, k, 64));
+    wave_hi_min = min(wave_hi_min, __shfl_xor(wave_hi_min, k, 64));
+  }
+  const bool wave_active = (wave * 32) < it.nrows;
 
   bf16x8 qop[NS];
   {
@@ -85,134 +104,188 @@ __global__ __launch_bounds__(256) void attn_large_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.score_scale;
 
   const int ebytes = FP8 ? 1 : 2;
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * ebytes;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * ebytes;
   const int32_t bmask = (1 << a.log2B) - 1;
-  const int tid = threadIdx.x;
+  const int nb = (it.kv_end - it.kv_begin + kKB - 1) / kKB;
 
-  for (int tb = it.kv_begin; tb < it.kv_end; tb += kKB) {
-    __syncthreads();   // the previous block's LDS reads are done
-    if (tid < kKB) {
-      const int t = min(tb + tid, it.kv_end - 1);
-      const int64_t page = kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
-      const int64_t slot = t & bmask;
-      s_koff[tid] = (page * a.k_sp + slot * a.k_sb) * ebytes;
-      s_voff[tid] = (page * a.v_sp + slot * a.v_sb) * ebytes;
-    }
-    __syncthreads();
-    // ---- K: 64 rows x CPR chunks of 16 bytes (bf16) into the swizzled tile
-    if (FP8) {
-      // source chunk = 16 codes = two bf16 chunks
-      for (int q = tid; q < kKB * (CPR / 2); q += 256) {
-        const int t = q / (CPR / 2), c = q % (CPR / 2);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kbase + s_koff[t] + c * 16);
-        *reinterpret_cast<bf16x8*>(ks + 8 * k_pos<D>(t, 2 * c)) = e4m3x8_to_bf16x8(w[0], w[1]);
-        *reinterpret_cast<bf16x8*>(ks + 8 * k_pos<D>(t, 2 * c + 1)) = e4m3x8_to_bf16x8(w[2], w[3]);
-      }
-    } else {
+  // page id of this lane's token in block b (wave 0 only), clamped into the range
+  auto page_of = [&](int b) -> int64_t {
+    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
+    return kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
+  };
+  auto put_offsets = [&](int b, int64_t page, int buf) {
+    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
+    const int64_t slot = t & bmask;
+    s_koff[buf][lane] = (page * a.k_sp + slot * a.k_sb) * ebytes;
+    s_voff[buf][lane] = (page * a.v_sp + slot * a.v_sb) * ebytes;
+  };
+
+  // prefetch registers: K source chunks, V rows of one (group, chunk) pair
+  u32x4 kreg[KLD];
+  u32x4 vreg[4];
+  const int vu = tid & 15, vc = tid >> 4;   // V pair of this thread (valid if tid < VPAIRS)
+  auto load_block = [&](int buf) {
 #pragma unroll
-      for (int q = tid; q < kKB * CPR; q += 256) {
-        const int t = q / CPR, c = q % CPR;
-        const u32x4 w = *reinterpret_cast<const u32x4*>(kbase + s_koff[t] + c * 16);
-        *reinterpret_cast<u32x4*>(ks + 8 * k_pos<D>(t, c)) = w;
-      }
+    for (int k = 0; k < KLD; ++k) {
+      const int q = tid + 256 * k;
+      const int t = q / SCPR, cc = q % SCPR;
+      kreg[k] = *reinterpret_cast<const u32x4*>(kbase + s_koff[buf][t] + cc * 16);
     }
-    // ---- V: thread (u = 4-token group, c = 8-column chunk) -> 8 transposed 8-byte writes
-    for (int q = tid; q < (kKB / 4) * CPR; q += 256) {
-      const int u = q & 15, c = q >> 4;
-      uint32_t e[4][4];   // e[token][dword] = bf16 pairs of columns 8c .. 8c+7
+    if (tid < VPAIRS) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const char* src = vbase + s_voff[4 * u + j];
+        const char* src = vbase + s_voff[buf][4 * vu + j];
         if (FP8) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(src + c * 8);
-          const u32x4 b = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[0], w[1]));
+          const u32x2 w = *reinterpret_cast<const u32x2*>(src + vc * 8);
+          vreg[j] = u32x4{w[0], w[1], 0u, 0u};
+        } else {
+          vreg[j] = *reinterpret_cast<const u32x4*>(src + vc * 16);
+        }
+      }
+    }
+  };
+  auto store_block = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < KLD; ++k) {
+      const int q = tid + 256 * k;
+      const int t = q / SCPR, cc = q % SCPR;
+      if (FP8) {
+        *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc)]) =
+            e4m3x8_to_bf16x8(kreg[k][0], kreg[k][1]);
+        *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc + 1)]) =
+            e4m3x8_to_bf16x8(kreg[k][2], kreg[k][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(&ks[buf][8 * k_pos<D>(t, cc)]) = kreg[k];
+      }
+    }
+    if (tid < VPAIRS) {
+      uint32_t e[4][4];   // e[token][dword]: bf16 pairs of columns 8vc .. 8vc+7
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (FP8) {
+          const u32x4 b = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(vreg[j][0], vreg[j][1]));
 #pragma unroll
           for (int k = 0; k < 4; ++k) e[j][k] = b[k];
         } else {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(src + c * 16);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) e[j][k] = w[k];
+          for (int k = 0; k < 4; ++k) e[j][k] = vreg[j][k];
         }
       }
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        const int d = 8 * c + i;
-        const int sh = (i & 1) * 16;
-        const uint32_t v0 = (e[0][i >> 1] >> sh) & 0xffffu, v1 = (e[1][i >> 1] >> sh) & 0xffffu;
-        const uint32_t v2 = (e[2][i >> 1] >> sh) & 0xffffu, v3 = (e[3][i >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(vt + vt_pos(d, u)) = u32x2{v0 | (v1 << 16), v2 | (v3 << 16)};
+        const int d = 8 * vc + i;
+        uint32_t lo, hi;
+        if (i & 1) {
+          lo = __builtin_amdgcn_perm(e[1][i >> 1], e[0][i >> 1], 0x07060302u);
+          hi = __builtin_amdgcn_perm(e[3][i >> 1], e[2][i >> 1], 0x07060302u);
+        } else {
+          lo = __builtin_amdgcn_perm(e[1][i >> 1], e[0][i >> 1], 0x05040100u);
+          hi = __builtin_amdgcn_perm(e[3][i >> 1], e[2][i >> 1], 0x05040100u);
+        }
+        *reinterpret_cast<u32x2*>(&vt[buf][vt_pos(d, vu)]) = u32x2{lo, hi};
       }
     }
-    __syncthreads();
+  };
 
-    // ---- S^T = K Q^T: two 32-token tiles
-    f32x16 sacc[2];
+  // ---- prologue: offsets of blocks 0 and 1, block 0 staged, page ids of block 2 in flight
+  int64_t page_next = 0;
+  if (wave == 0) {
+    put_offsets(0, page_of(0), 0);
+    if (nb > 1) put_offsets(1, page_of(1), 1);
+    if (nb > 2) page_next = page_of(2);
+  }
+  __syncthreads();
+  load_block(0);
+  store_block(0);
+  __syncthreads();
+
+  for (int b = 0; b < nb; ++b) {
+    const int cur = b & 1;
+    const int tb = it.kv_begin + b * kKB;
+    if (b + 1 < nb) load_block(cur ^ 1);   // lands while this block is computed
+
+    if (wave_active) {
+      // ---- S^T = K Q^T: two 32-token tiles
+      f32x16 sacc[2];
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
+      for (int T = 0; T < 2; ++T) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[T][i] = 0.f;
-      const int t = 32 * T + n32;
+        for (int i = 0; i < 16; ++i) sacc[T][i] = 0.f;
+        const int t = 32 * T + n32;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(ks + 8 * k_pos<D>(t, 2 * s + hf));
-        sacc[T] = mfma32(kop, qop[s], sacc[T]);
+        for (int s = 0; s < NS; ++s) {
+          const bf16x8 kop =
+              *reinterpret_cast<const bf16x8*>(&ks[cur][8 * k_pos<D>(t, 2 * s + hf)]);
+          sacc[T] = mfma32(kop, qop[s], sacc[T]);
+        }
       }
-    }
-    // ---- online softmax; element i of tile T is token 32T + 8(i/4) + 4hf + i%4
-    float mb = -INFINITY;
+      // ---- mask (boundary blocks only); element i of tile T is token 32T + 8(i/4) + 4hf + i%4
+      const bool need_mask = (tb < wave_lo_max) | (tb + kKB > wave_hi_min);
+      if (need_mask) {
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+        for (int T = 0; T < 2; ++T)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = tb + 32 * T + 8 * (i >> 2) + 4 * hf + (i & 3);
-        const bool vis = (t >= row_lo) & (t < row_hi);
-        sacc[T][i] = vis ? sacc[T][i] * a.score_scale : -INFINITY;
-        mb = fmaxf(mb, sacc[T][i]);
+          for (int i = 0; i < 16; ++i) {
+            const int t = tb + 32 * T + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (!((t >= row_lo) & (t < row_hi))) sacc[T][i] = -INFINITY;
+          }
       }
-    mb = fmaxf(mb, shfl_xor_f(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    float alpha = 1.f, psum = 0.f;
-    if (m_new == -INFINITY) {
+      float mb = -INFINITY;
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[T][i] = 0.f;
-    } else {
-      alpha = exp2f(m_run - m_new);
+        for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[T][i]);
+      mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;       // block max in base-2 units
+      // raise the reference max only when the block exceeds it by kLazy
+      const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+      if (__any(m_new != m_run)) {
+        const float alpha = fast_exp2(m_run - m_new);   // 0 when m_run was -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sacc[T][i] = exp2f(sacc[T][i] - m_new);
+          sacc[T][i] = fast_exp2(__builtin_fmaf(sacc[T][i], c, -msub));
           psum += sacc[T][i];
         }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+      l_run += psum;
+      // ---- O^T += V^T P^T over four 16-token k-steps
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int kk = 0; kk < 4; ++kk) {
+        const int T = kk >> 1, i0 = 8 * (kk & 1);
+        u32x4 pw;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-    // ---- O^T += V^T P^T over four 16-token k-steps
+        for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[T][i0 + 2 * h], sacc[T][i0 + 2 * h + 1]);
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int T = kk >> 1, i0 = 8 * (kk & 1);
-      u32x4 pw;
-#pragma unroll
-      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[T][i0 + 2 * h], sacc[T][i0 + 2 * h + 1]);
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int d = 32 * dt + n32;
-        const u32x2 lo = *reinterpret_cast<const u32x2*>(vt + vt_pos(d, 4 * kk + hf));
-        const u32x2 hi = *reinterpret_cast<const u32x2*>(vt + vt_pos(d, 4 * kk + 2 + hf));
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-        oacc[dt] = mfma32(vop, pop, oacc[dt]);
+        for (int dt = 0; dt < NDT; ++dt) {
+          const int d = 32 * dt + n32;
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + hf)]);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + 2 + hf)]);
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+          oacc[dt] = mfma32(vop, pop, oacc[dt]);
+        }
       }
     }
+
+    if (b + 1 < nb) store_block(cur ^ 1);
+    if (wave == 0 && b + 2 < nb) {
+      put_offsets(b + 2, page_next, cur);        // block b's offsets are no longer read
+      if (b + 3 < nb) page_next = page_of(b + 3);
+    }
+    __syncthreads();
   }
 
   // ---- finalise: O^T element i of tile dt is column d = 32dt + 8(i/4) + 4hf + i%4

@@ -184,12 +184,12 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) p[T][i] = 0.f;
     } else {
-      alpha = exp2f(m_run - m_new);
+      alpha = fast_exp2(m_run - m_new);
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[T][i] = exp2f(x[T][i] - m_new);
+          p[T][i] = fast_exp2(x[T][i] - m_new);
           psum += p[T][i];
         }
     }
@@ -260,7 +260,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     float wt[kWaves];
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      wt[w] = exp2f(cm[w * 16 + row] - M);
+      wt[w] = fast_exp2(cm[w * 16 + row] - M);
       den += wt[w] * cl[w * 16 + row];
     }
 #pragma unroll

@@ -20,19 +20,27 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // ------------------------------------------------------------ conversions
 
-// binary32 -> bfloat16 bits, round to nearest even (finite inputs).
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+
+// binary32 -> bfloat16 bits, round to nearest even (gfx950 converts in hardware,
+// v_cvt_pk_bf16_f32, in the default round-to-nearest-even mode).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;   // NaN
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
-// Two bf16 bit patterns (lo, hi) packed in one dword.
+// Two bf16 values (lo, hi) packed in one dword, one conversion instruction.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  bf16x2 r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
 }
+
+// 2^x on the transcendental unit without the library's denormal-range fix-up:
+// callers pass x <= 0, where results below 2^-126 do not matter.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Value of an OCP E4M3 ("fn") code as binary32.  Exact: every E4M3 value is a
 // binary32 value.  Built from the fields (bias 7, subnormals m * 2^-9).

@@ -2,6 +2,7 @@
 // kernel sequencing for ak_run, diagnostics.  Declarations and contracts are
 // in include/ak.h.
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -191,10 +192,88 @@ extern "C" ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v,
 
 // -------------------------------------------------------------------- plan
 
-// The host copy of the uploaded metadata lives as long as the plan, so the
-// asynchronous upload never reads freed memory.
+// Plan workspaces (device buffer + pinned host staging for the upload) are
+// recycled through a small per-process pool: a plan is built once per step, and
+// a fresh hipMalloc / hipFree per step would cost milliseconds and synchronise
+// the device.  A workspace returns to the pool with an event recorded after the
+// last work that used it (its upload and every ak_run); it is handed out again
+// only once that event has completed, so reuse never races in-flight kernels.
+namespace ak {
+namespace {
+
+struct Workspace {
+  void* dev = nullptr;
+  size_t dev_bytes = 0;
+  void* host = nullptr;     // pinned
+  size_t host_bytes = 0;
+  hipEvent_t done = nullptr;
+  int device = 0;
+};
+
+constexpr size_t kPoolMax = 8;
+std::mutex g_pool_mu;
+std::vector<Workspace> g_pool;
+
+void release_ws(Workspace& w) {
+  if (w.dev) (void)hipFree(w.dev);
+  if (w.host) (void)hipHostFree(w.host);
+  if (w.done) (void)hipEventDestroy(w.done);
+  w = Workspace{};
+}
+
+// A workspace with at least the requested sizes on `device`, or an error.
+ak_status acquire_ws(int device, size_t dev_bytes, size_t host_bytes, Workspace* out) {
+  {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    for (size_t i = 0; i < g_pool.size(); ++i) {
+      Workspace& w = g_pool[i];
+      if (w.device != device || w.dev_bytes < dev_bytes || w.host_bytes < host_bytes) continue;
+      if (w.done && hipEventQuery(w.done) != hipSuccess) continue;
+      *out = w;
+      g_pool.erase(g_pool.begin() + i);
+      return AK_OK;
+    }
+  }
+  Workspace w;
+  w.device = device;
+  // round up so later, slightly larger batches can reuse the buffer
+  w.dev_bytes = std::max<size_t>(align256(dev_bytes + dev_bytes / 4), 1 << 16);
+  w.host_bytes = std::max<size_t>(align256(host_bytes + host_bytes / 4), 1 << 16);
+  hipError_t e = hipMalloc(&w.dev, w.dev_bytes);
+  if (e != hipSuccess) {
+    release_ws(w);
+    return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan: device workspace")
+                                    : hip_fail(e, "ak_plan: hipMalloc");
+  }
+  e = hipHostMalloc(&w.host, w.host_bytes, hipHostMallocDefault);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    release_ws(w);
+    return hip_fail(e, "ak_plan: pinned staging / event");
+  }
+  *out = w;
+  return AK_OK;
+}
+
+void return_ws(Workspace& w) {
+  if (!w.dev) return;
+  std::lock_guard<std::mutex> lk(g_pool_mu);
+  g_pool.push_back(w);
+  if (g_pool.size() > kPoolMax) {
+    // drop the oldest entry; its event says whether its last use is finished
+    Workspace old = g_pool.front();
+    g_pool.erase(g_pool.begin());
+    if (old.done) (void)hipEventSynchronize(old.done);
+    release_ws(old);
+  }
+  w = Workspace{};
+}
+
+}  // namespace
+}  // namespace ak
+
 struct ak_plan_private : ak_plan_t {
-  std::vector<unsigned char> stage;
+  ak::Workspace ws;
 };
 
 extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -246,12 +325,12 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const size_t meta = b_req + b_small + b_large + b_merge;
     p->d_bytes = meta + b_po + b_pl;
     if (p->d_bytes > 0) {
-      hipError_t e = hipMalloc(&p->d_buf, p->d_bytes);
-      if (e != hipSuccess) {
+      st = acquire_ws(dev, p->d_bytes, meta, &p->ws);
+      if (st != AK_OK) {
         delete p;
-        return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan: device workspace")
-                                        : hip_fail(e, "ak_plan: hipMalloc");
+        return st;
       }
+      p->d_buf = p->ws.dev;
       unsigned char* base = static_cast<unsigned char*>(p->d_buf);
       p->d_reqs = reinterpret_cast<Req*>(base);
       p->d_small = reinterpret_cast<Item*>(base + b_req);
@@ -259,14 +338,7 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
       p->d_part_o = reinterpret_cast<float*>(base + meta);
       p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
-      try {
-        p->stage.assign(meta, 0);
-      } catch (const std::bad_alloc&) {
-        (void)hipFree(p->d_buf);
-        delete p;
-        return fail(AK_ERR_OOM, "ak_plan: out of host memory");
-      }
-      unsigned char* h = p->stage.data();
+      unsigned char* h = static_cast<unsigned char*>(p->ws.host);
       if (!p->reqs.empty()) std::memcpy(h, p->reqs.data(), p->reqs.size() * sizeof(Req));
       if (!p->small_items.empty())
         std::memcpy(h + b_req, p->small_items.data(), p->small_items.size() * sizeof(Item));
@@ -276,13 +348,14 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
         std::memcpy(h + b_req + b_small + b_large, p->merges.data(),
                     p->merges.size() * sizeof(MergeJob));
       hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
-      if (meta > 0) {
-        e = hipMemcpyAsync(p->d_buf, h, meta, hipMemcpyHostToDevice, s);
-        if (e != hipSuccess) {
-          (void)hipFree(p->d_buf);
-          delete p;
-          return hip_fail(e, "ak_plan: upload");
-        }
+      hipError_t e = hipSuccess;
+      if (meta > 0) e = hipMemcpyAsync(p->d_buf, h, meta, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipEventRecord(p->ws.done, s);
+      if (e != hipSuccess) {
+        (void)hipStreamSynchronize(s);
+        return_ws(p->ws);
+        delete p;
+        return hip_fail(e, "ak_plan: upload");
       }
     }
   }
@@ -292,8 +365,9 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
 extern "C" void ak_plan_destroy(ak_plan_t* plan) {
   if (!plan) return;
-  if (plan->d_buf) (void)hipFree(plan->d_buf);
-  delete static_cast<ak_plan_private*>(plan);
+  auto* pp = static_cast<ak_plan_private*>(plan);
+  return_ws(pp->ws);     // the workspace's event covers its last use
+  delete pp;
 }
 
 // --------------------------------------------------------------------- run
@@ -426,6 +500,12 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
       e = launch_merge(m, p->D, qd, s);
     }
     if (e != hipSuccess) return hip_fail(e, "ak_run: merge");
+  }
+  // the plan's workspace may be recycled only after this run has finished
+  const auto* pp = static_cast<const ak_plan_private*>(p);
+  if (pp->ws.done) {
+    e = hipEventRecord(pp->ws.done, s);
+    if (e != hipSuccess) return hip_fail(e, "ak_run: event record");
   }
   return AK_OK;
 }
