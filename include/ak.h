@@ -143,7 +143,10 @@ typedef struct {
  *   plan           receives the new plan.
  *
  * The plan reads only host arrays (no device read-back) and makes one
- * host-to-device copy of its work list.  Supported: num_qo_heads a multiple of
+ * host-to-device copy of its work list.  Its device workspace and pinned
+ * staging come from a small per-process pool of recycled workspaces; when the
+ * host has more than 16 plans' work still queued on the device, ak_plan waits
+ * for the oldest of it to finish before reusing its workspace.  Supported: num_qo_heads a multiple of
  * num_kv_heads with a group of 1, 2, 4, 8 or 16; head_dim 64 or 128; page_size
  * a power of two in [1, 256].  Errors: AK_ERR_INVALID_ARG, AK_ERR_UNSUPPORTED,
  * AK_ERR_BAD_INDPTR (qo/kv indptr not starting at 0 or decreasing),
@@ -225,6 +228,14 @@ ak_status ak_plan_export(const ak_plan_t* plan, int32_t* items, int64_t capacity
  * `slots` is a device int64 array of at least sum_r L_r entries.  Uses the same
  * device-side address arithmetic as ak_run.  Errors: AK_ERR_INVALID_ARG, AK_ERR_HIP. */
 ak_status ak_gather_slots(const ak_plan_t* plan, int64_t* slots, void* stream);
+
+/* ak_fp8_to_bf16 -- the cache's FP8 E4M3 decode, materialised (diagnostics).
+ * Widens n E4M3 codes (device uint8 array, n a multiple of 8) into bf16 bit
+ * patterns (device uint16 array of n entries) with the conversion the attention
+ * kernels apply to FP8 K/V rows before their MFMA (exact, scale 1).
+ * Errors: AK_ERR_INVALID_ARG (null pointer, n < 0 or not a multiple of 8),
+ * AK_ERR_HIP. */
+ak_status ak_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream);
 
 /* Per-kernel timing with HIP events on the launch stream (diagnostics).
  * ak_profile_enable(1) records an event pair around every kernel the library

@@ -43,7 +43,7 @@ AK_PLAN_HOST_ONLY = 1
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
-            "ak_profile_read", "ak_version"]
+            "ak_profile_read", "ak_version", "ak_fp8_to_bf16"]
 
 
 class AkError(RuntimeError):
@@ -92,6 +92,8 @@ def _load():
     lib.ak_profile_enable.restype = ctypes.c_int
     lib.ak_profile_read.argtypes = [P(ctypes.c_int64), P(ctypes.c_double), ctypes.c_int32]
     lib.ak_profile_read.restype = ctypes.c_int
+    lib.ak_fp8_to_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+    lib.ak_fp8_to_bf16.restype = ctypes.c_int
     lib.ak_version.argtypes = []
     lib.ak_version.restype = ctypes.c_char_p
     return lib
@@ -286,3 +288,15 @@ def ak_profile_read() -> dict:
     ms = (ctypes.c_double * n)()
     _check(_lib.ak_profile_read(launches, ms, n))
     return {k: (int(launches[i]), float(ms[i])) for i, k in enumerate(KERNEL_KINDS)}
+
+
+def ak_fp8_to_bf16(codes, out=None, stream=None):
+    """Widen device uint8 E4M3 codes (numel a multiple of 8) to bf16 with the
+    kernels' conversion; returns a bfloat16 tensor."""
+    import torch
+
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.bfloat16, device=codes.device)
+    _check(_lib.ak_fp8_to_bf16(ctypes.c_void_p(codes.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                               codes.numel(), _stream_ptr(stream)))
+    return out

@@ -9,20 +9,27 @@
 // heads of one KV head share every K/V byte, so they form one tile).
 //
 // gfx950 mapping.  One workgroup (4 waves) per work item; wave w takes the
-// item's 32-token blocks w, w+4, ...  Per block:
+// item's 32-token blocks w, w+4, ...  Each wave runs a two-stage register
+// pipeline: while block k is computed, block k+1's K and V rows are in flight
+// into a second register set, and the page ids of block k+2 are in flight too,
+// so every wave keeps two blocks of HBM reads outstanding.  Per block:
 //   S^T (32 tokens x 16 rows) = K (tokens x D) * Q^T   two 16x16x32 bf16 MFMA
 //     tiles per 32 d; K rows go straight from HBM into the MFMA A operand
 //     (each lane loads 32 contiguous bytes of one token row per step pair);
 //   online softmax per row in base 2 (the scale carries log2(e)); a row lives in
-//     the 4 lanes l%16 = row, so its max needs two xor-shuffles;
+//     the 4 lanes l%16 = row, so its max needs two xor-shuffles; the reference
+//     max is raised only when a block exceeds it by more than 2^8;
 //   O^T (D x 16 rows) += V^T * P^T   one 16x16x32 MFMA per 16 d; P stays in the
 //     registers the S^T tile produced it in, V is staged through LDS and read
 //     column-wise.
 // The d order inside a 32-wide k-step is permuted identically for K and Q
 // (contraction order is free), and the token order inside PV's k-steps follows
-// the S^T register layout identically for P and V.
+// the S^T register layout identically for P and V.  FP8 rows are widened to
+// bf16 in registers (exact, two codes per instruction).
 // The 4 waves' (m, l, O) states are merged in LDS at the end; the item writes
 // the final output or, for a split, its normalised partial and base-2 LSE.
+
+#include <climits>
 
 #include "ak_launch.h"
 
@@ -31,7 +38,8 @@ namespace ak {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBlk = 32;   // tokens per wave block
+constexpr int kBlk = 32;         // tokens per wave block
+constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
 
 template <int D>
 __device__ __forceinline__ int dmap(int s, int g4) {
@@ -40,7 +48,19 @@ __device__ __forceinline__ int dmap(int s, int g4) {
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
+struct Blk {
+  static constexpr int NSTEP = D / 32;
+  static constexpr int KL = FP8 ? (NSTEP + 1) / 2 : NSTEP;          // 16-byte K loads per tile
+  static constexpr int CPR = (D * (FP8 ? 1 : 2)) / 16;              // 16-byte chunks per V row
+  static constexpr int TPI = 64 / CPR;                              // V tokens per load instruction
+  static constexpr int VL = kBlk / TPI;                             // 16-byte V loads per lane
+  u32x4 k[2][KL];
+  u32x4 v[VL];
+};
+
+template <int D, bool FP8>
+__global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
+  using B = Blk<D, FP8>;
   constexpr int NSTEP = D / 32;       // S^T k-steps
   constexpr int NDT = D / 16;         // O^T d-tiles
   constexpr int VROW = D + 4;         // bf16 per staged V row (pad: conflict-free column reads)
@@ -69,6 +89,13 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
   if (a.causal) row_hi = min(row_hi, qpos + 1);
   if (!rvalid) row_lo = row_hi = 0;
+  // blocks inside [wave_lo_max, wave_hi_min) need no mask (rows past nrows are never written)
+  int wave_lo_max = rvalid ? row_lo : INT_MIN, wave_hi_min = rvalid ? row_hi : INT_MAX;
+#pragma unroll
+  for (int k = 1; k < 16; k <<= 1) {
+    wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, k, 64));
+    wave_hi_min = min(wave_hi_min, __shfl_xor(wave_hi_min, k, 64));
+  }
 
   bf16x8 qop[NSTEP];
   {
@@ -87,69 +114,68 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < NDT; ++i) oacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.score_scale;
 
   const int32_t kv_begin = it.kv_begin, kv_end = it.kv_end;
   const int nblk = (kv_end - kv_begin + kBlk - 1) / kBlk;
+  const int nloc = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;   // this wave's blocks
   const int32_t bmask = (1 << a.log2B) - 1;
-  const int ebytes = FP8 ? 1 : 2;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * ebytes;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * ebytes;
+  constexpr int EB = FP8 ? 1 : 2;
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * EB;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * EB;
+  const int64_t kps = a.k_sp * EB, kbs = a.k_sb * EB, vps = a.v_sp * EB, vbs = a.v_sb * EB;
   __bf16* vs = reinterpret_cast<__bf16*>(smem) + wave * kBlk * VROW;
 
-  for (int b = wave; b < nblk; b += kWaves) {
-    const int tb = kv_begin + b * kBlk;
-    // byte offsets of this block's 32 token rows: lane l computes token tb + (l & 31)
-    int64_t my_koff, my_voff;
-    {
-      const int t = min(tb + (lane & 31), kv_end - 1);
-      const int64_t page = kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
-      const int64_t slot = t & bmask;
-      my_koff = (page * a.k_sp + slot * a.k_sb) * ebytes;
-      my_voff = (page * a.v_sp + slot * a.v_sb) * ebytes;
-    }
-    // ---- K straight into MFMA A-operand registers
-    bf16x8 kop[2][NSTEP];
+  // page id of this lane's token (lane & 31) in local block k
+  auto page_for = [&](int k) -> int32_t {
+    const int t = min(kv_begin + (wave + kWaves * k) * kBlk + (lane & 31), kv_end - 1);
+    return (int32_t)kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
+  };
+  // issue the HBM reads of local block k (page ids of its tokens in `pg`)
+  auto load_blk = [&](B& blk, int32_t pg, int k) {
+    const int tb = kv_begin + (wave + kWaves * k) * kBlk;
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-      const int64_t off = __shfl(my_koff, 16 * T + n16, 64);
-      const char* row = kbase + off;
+      const int tt = 16 * T + n16;
+      const int t = min(tb + tt, kv_end - 1);
+      const int64_t page = __shfl(pg, tt, 64);
+      const char* row = kbase + page * kps + (int64_t)(t & bmask) * kbs;
 #pragma unroll
-      for (int p = 0; p < NSTEP / 2 + (NSTEP == 1); ++p) {
-        const int d0 = 64 * p + 16 * g4;
-        if (FP8) {
-          const u32x4 w = *reinterpret_cast<const u32x4*>(row + d0);
-          kop[T][2 * p] = e4m3x8_to_bf16x8(w[0], w[1]);
-          kop[T][2 * p + 1] = e4m3x8_to_bf16x8(w[2], w[3]);
-        } else {
-          const bf16x8* r = reinterpret_cast<const bf16x8*>(row + d0 * 2);
-          kop[T][2 * p] = r[0];
-          kop[T][2 * p + 1] = r[1];
-        }
+      for (int p = 0; p < B::KL; ++p) {
+        const int d0 = FP8 ? 64 * p + 16 * g4 : dmap<D>(p, g4);
+        blk.k[T][p] = *reinterpret_cast<const u32x4*>(row + d0 * EB);
       }
     }
-    // ---- V rows into LDS (bf16), whole rows per 16-byte chunk
-    {
-      constexpr int CPR = FP8 ? D / 16 : D / 8;   // 16-byte chunks per source row
-      constexpr int TPI = 64 / CPR;               // tokens per load instruction
-      const int c = lane % CPR;
+    const int cidx = lane % B::CPR;
 #pragma unroll
-      for (int i = 0; i < kBlk / TPI; ++i) {
-        const int tt = i * TPI + lane / CPR;
-        const int64_t off = __shfl(my_voff, tt, 64);
-        const u32x4 w = *reinterpret_cast<const u32x4*>(vbase + off + c * 16);
-        // staged rows are 8-byte aligned (VROW pad), so write in 8-byte pieces
+    for (int i = 0; i < B::VL; ++i) {
+      const int tt = i * B::TPI + lane / B::CPR;
+      const int t = min(tb + tt, kv_end - 1);
+      const int64_t page = __shfl(pg, tt, 64);
+      blk.v[i] = *reinterpret_cast<const u32x4*>(vbase + page * vps + (int64_t)(t & bmask) * vbs +
+                                                 cidx * 16);
+    }
+  };
+  // attention over local block k held in `blk`
+  auto compute_blk = [&](const B& blk, int k) {
+    const int tb = kv_begin + (wave + kWaves * k) * kBlk;
+    // ---- V rows into this wave's LDS stage (8-byte pieces: staged rows are 8-byte aligned)
+    {
+      const int cidx = lane % B::CPR;
+#pragma unroll
+      for (int i = 0; i < B::VL; ++i) {
+        const int tt = i * B::TPI + lane / B::CPR;
+        u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + cidx * (FP8 ? 16 : 8));
         if (FP8) {
-          const u32x4 lo = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[0], w[1]));
-          const u32x4 hi = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[2], w[3]));
-          u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + c * 16);
+          const u32x4 lo = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(blk.v[i][0], blk.v[i][1]));
+          const u32x4 hi = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(blk.v[i][2], blk.v[i][3]));
           dst[0] = u32x2{lo[0], lo[1]};
           dst[1] = u32x2{lo[2], lo[3]};
           dst[2] = u32x2{hi[0], hi[1]};
           dst[3] = u32x2{hi[2], hi[3]};
         } else {
-          u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + c * 8);
-          dst[0] = u32x2{w[0], w[1]};
-          dst[1] = u32x2{w[2], w[3]};
+          dst[0] = u32x2{blk.v[i][0], blk.v[i][1]};
+          dst[1] = u32x2{blk.v[i][2], blk.v[i][3]};
         }
       }
     }
@@ -159,53 +185,57 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     for (int T = 0; T < 2; ++T) {
       sacc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int s = 0; s < NSTEP; ++s) sacc[T] = mfma16(kop[T][s], qop[s], sacc[T]);
-    }
-    // ---- online softmax (base 2), rows = lane % 16
-    float x[2][4];
-    float mb = -INFINITY;
-#pragma unroll
-    for (int T = 0; T < 2; ++T)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = tb + 16 * T + 4 * g4 + i;
-        const bool vis = (t >= row_lo) & (t < row_hi);
-        x[T][i] = vis ? sacc[T][i] * a.score_scale : -INFINITY;
-        mb = fmaxf(mb, x[T][i]);
+      for (int s = 0; s < NSTEP; ++s) {
+        bf16x8 kop;
+        if (FP8) {
+          const u32x4& w = blk.k[T][s >> 1];
+          kop = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
+        } else {
+          kop = __builtin_bit_cast(bf16x8, blk.k[T][s]);
+        }
+        sacc[T] = mfma16(kop, qop[s], sacc[T]);
       }
-    mb = fmaxf(mb, shfl_xor_f(mb, 16));
-    mb = fmaxf(mb, shfl_xor_f(mb, 32));
-    const float m_new = fmaxf(m_run, mb);
-    float p[2][4];
-    float alpha = 1.f, psum = 0.f;
-    if (m_new == -INFINITY) {
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p[T][i] = 0.f;
-    } else {
-      alpha = fast_exp2(m_run - m_new);
+    }
+    // ---- online softmax (base 2), rows = lane % 16; element i of tile T is token 16T + 4g4 + i
+    if ((tb < wave_lo_max) | (tb + kBlk > wave_hi_min)) {
 #pragma unroll
       for (int T = 0; T < 2; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[T][i] = fast_exp2(x[T][i] - m_new);
-          psum += p[T][i];
+          const int t = tb + 16 * T + 4 * g4 + i;
+          if (!((t >= row_lo) & (t < row_hi))) sacc[T][i] = -INFINITY;
         }
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
+    float mb = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mb = fmaxf(mb, shfl_xor_f(mb, 16));
+    mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;
+    const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+    if (__any(m_new != m_run)) {
+      const float alpha = fast_exp2(m_run - m_new);   // 0 when m_run was -inf
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
+      for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+        for (int i = 0; i < 4; ++i) oacc[dt][i] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+    float p[2][4];
+#pragma unroll
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[T][i] = fast_exp2(__builtin_fmaf(sacc[T][i], c, -msub));
+        l_run += p[T][i];
+      }
     u32x4 pw;
     pw[0] = pack_bf16x2(p[0][0], p[0][1]);
     pw[1] = pack_bf16x2(p[0][2], p[0][3]);
     pw[2] = pack_bf16x2(p[1][0], p[1][1]);
     pw[3] = pack_bf16x2(p[1][2], p[1][3]);
     const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-    // V staging is private to this wave: wait for its LDS writes (and keep the
+    // the V stage is private to this wave: wait for its LDS writes (and keep the
     // compiler from moving LDS accesses across this point)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     // ---- O^T += V^T P^T ; k-slot 8*g4 + jj <-> token 16*(jj/4) + 4*g4 + jj%4
@@ -225,6 +255,27 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     }
     // the next block's staging writes must not pass this block's reads
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
+  // ---- two-stage pipeline over this wave's blocks (ping-pong register sets)
+  if (nloc > 0) {
+    B b0, b1;
+    int32_t pg1 = nloc > 1 ? page_for(1) : 0;
+    int32_t pg2 = nloc > 2 ? page_for(2) : 0;
+    load_blk(b0, page_for(0), 0);
+    for (int k = 0; k < nloc; k += 2) {
+      if (k + 1 < nloc) {
+        load_blk(b1, pg1, k + 1);
+        if (k + 3 < nloc) pg1 = page_for(k + 3);
+      }
+      compute_blk(b0, k);
+      if (k + 1 >= nloc) break;
+      if (k + 2 < nloc) {
+        load_blk(b0, pg2, k + 2);
+        if (k + 4 < nloc) pg2 = page_for(k + 4);
+      }
+      compute_blk(b1, k + 1);
+    }
   }
 
   // ---- combine the 4 waves' states
@@ -253,7 +304,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + row]);
   float o[CPT];
 #pragma unroll
-  for (int c = 0; c < CPT; ++c) o[c] = 0.f;
+  for (int cc = 0; cc < CPT; ++cc) o[cc] = 0.f;
   float lse2 = -INFINITY;
   if (M != -INFINITY) {
     float den = 0.f;
@@ -266,10 +317,10 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
     for (int w = 0; w < kWaves; ++w)
 #pragma unroll
-      for (int c = 0; c < CPT; ++c) o[c] += wt[w] * co[(w * 16 + row) * ORW + c0 + c];
+      for (int cc = 0; cc < CPT; ++cc) o[cc] += wt[w] * co[(w * 16 + row) * ORW + c0 + cc];
     const float inv = a.v_scale / den;
 #pragma unroll
-    for (int c = 0; c < CPT; ++c) o[c] *= inv;
+    for (int cc = 0; cc < CPT; ++cc) o[cc] *= inv;
     lse2 = M + log2f(den);
   }
   const int rrho = it.row0 + row;
@@ -280,7 +331,7 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     uint16_t* op = static_cast<uint16_t*>(a.out) + rtok * a.o_st + (int64_t)rhead * a.o_sh + c0;
     u32x4 w4;
 #pragma unroll
-    for (int c = 0; c < CPT; c += 2) w4[c / 2] = pack_bf16x2(o[c], o[c + 1]);
+    for (int cc = 0; cc < CPT; cc += 2) w4[cc / 2] = pack_bf16x2(o[cc], o[cc + 1]);
     if (CPT == 8) {
       *reinterpret_cast<u32x4*>(op) = w4;
     } else {
@@ -291,7 +342,8 @@ __global__ __launch_bounds__(256) void attn_small_kernel(AttnArgs a) {
     const int64_t prow = (int64_t)it.pbase + row;
     float* pp = a.part_o + prow * D + c0;
 #pragma unroll
-    for (int c = 0; c < CPT; c += 4) *reinterpret_cast<f32x4*>(pp + c) = f32x4{o[c], o[c + 1], o[c + 2], o[c + 3]};
+    for (int cc = 0; cc < CPT; cc += 4)
+      *reinterpret_cast<f32x4*>(pp + cc) = f32x4{o[cc], o[cc + 1], o[cc + 2], o[cc + 3]};
     if ((threadIdx.x & 15) == 0) a.part_lse[prow] = lse2;
   }
 }

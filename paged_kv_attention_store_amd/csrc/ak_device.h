@@ -42,21 +42,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 // callers pass x <= 0, where results below 2^-126 do not matter.
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Value of an OCP E4M3 ("fn") code as binary32.  Exact: every E4M3 value is a
-// binary32 value.  Built from the fields (bias 7, subnormals m * 2^-9).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
-  const uint32_t s = (c & 0x80u) << 24;
-  const uint32_t e = (c >> 3) & 0xfu;
-  const uint32_t m = c & 7u;
-  float mag;
-  if (e == 0) {
-    mag = (float)m * 0.001953125f;                       // m * 2^-9
-  } else {
-    mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  }
-  return __uint_as_float(__float_as_uint(mag) | s);
-}
-
 // binary32 value (already divided by the scale) -> E4M3 code: nearest, ties to
 // even, saturating at +-448, sign kept.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
@@ -81,21 +66,15 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
   return mag | sign;
 }
 
-// Eight consecutive E4M3 codes (two dwords) -> eight bf16 (exact) as bf16x8.
+// Eight consecutive E4M3 codes (two dwords, code 0 in the low byte) -> eight
+// bf16 values, exact.  gfx950 converts two codes per instruction
+// (v_cvt_scalef32_pk_bf16_fp8, OCP E4M3, scale 1).
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  u32x4 r;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const uint32_t w = h ? hi : lo;
-    // f32 of an E4M3 value has at most 4 significant bits: truncating to bf16 is exact.
-    const uint32_t b0 = __float_as_uint(e4m3_to_f32(w & 0xffu)) >> 16;
-    const uint32_t b1 = __float_as_uint(e4m3_to_f32((w >> 8) & 0xffu)) >> 16;
-    const uint32_t b2 = __float_as_uint(e4m3_to_f32((w >> 16) & 0xffu)) >> 16;
-    const uint32_t b3 = __float_as_uint(e4m3_to_f32(w >> 24)) >> 16;
-    r[2 * h] = b0 | (b1 << 16);
-    r[2 * h + 1] = b2 | (b3 << 16);
-  }
-  return __builtin_bit_cast(bf16x8, r);
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // ------------------------------------------------------------------ MFMA

@@ -25,6 +25,8 @@ hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int
                                int32_t R, int32_t log2B, int64_t num_pages, int64_t* slots,
                                hipStream_t s);
 
+hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t s);
+
 // kv dtype: AK_BF16 or AK_FP8_E4M3 for bf16 queries.
 hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s);
 hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s);

@@ -210,9 +210,9 @@ struct Workspace {
   int device = 0;
 };
 
-constexpr size_t kPoolMax = 8;
+constexpr size_t kPoolMax = 16;
 std::mutex g_pool_mu;
-std::vector<Workspace> g_pool;
+std::vector<Workspace> g_pool;   // oldest first
 
 void release_ws(Workspace& w) {
   if (w.dev) (void)hipFree(w.dev);
@@ -221,51 +221,82 @@ void release_ws(Workspace& w) {
   w = Workspace{};
 }
 
-// A workspace with at least the requested sizes on `device`, or an error.
-ak_status acquire_ws(int device, size_t dev_bytes, size_t host_bytes, Workspace* out) {
-  {
-    std::lock_guard<std::mutex> lk(g_pool_mu);
-    for (size_t i = 0; i < g_pool.size(); ++i) {
-      Workspace& w = g_pool[i];
-      if (w.device != device || w.dev_bytes < dev_bytes || w.host_bytes < host_bytes) continue;
-      if (w.done && hipEventQuery(w.done) != hipSuccess) continue;
-      *out = w;
-      g_pool.erase(g_pool.begin() + i);
-      return AK_OK;
+// (Re)allocate the buffers of `w` to at least the requested sizes.  `w` must be
+// idle (its event completed).
+ak_status size_ws(Workspace& w, size_t dev_bytes, size_t host_bytes) {
+  if (w.dev_bytes < dev_bytes) {
+    if (w.dev) (void)hipFree(w.dev);
+    w.dev = nullptr;
+    // round up so later, slightly larger batches fit
+    w.dev_bytes = std::max<size_t>(align256(dev_bytes + dev_bytes / 4), 1 << 16);
+    hipError_t e = hipMalloc(&w.dev, w.dev_bytes);
+    if (e != hipSuccess) {
+      w.dev_bytes = 0;
+      return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan: device workspace")
+                                      : hip_fail(e, "ak_plan: hipMalloc");
     }
   }
-  Workspace w;
-  w.device = device;
-  // round up so later, slightly larger batches can reuse the buffer
-  w.dev_bytes = std::max<size_t>(align256(dev_bytes + dev_bytes / 4), 1 << 16);
-  w.host_bytes = std::max<size_t>(align256(host_bytes + host_bytes / 4), 1 << 16);
-  hipError_t e = hipMalloc(&w.dev, w.dev_bytes);
-  if (e != hipSuccess) {
-    release_ws(w);
-    return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan: device workspace")
-                                    : hip_fail(e, "ak_plan: hipMalloc");
+  if (w.host_bytes < host_bytes) {
+    if (w.host) (void)hipHostFree(w.host);
+    w.host = nullptr;
+    w.host_bytes = std::max<size_t>(align256(host_bytes + host_bytes / 4), 1 << 16);
+    hipError_t e = hipHostMalloc(&w.host, w.host_bytes, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      w.host_bytes = 0;
+      return hip_fail(e, "ak_plan: pinned staging");
+    }
   }
-  e = hipHostMalloc(&w.host, w.host_bytes, hipHostMallocDefault);
-  if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
-  if (e != hipSuccess) {
+  if (!w.done) {
+    hipError_t e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "ak_plan: event");
+  }
+  return AK_OK;
+}
+
+// A workspace of at least the requested sizes on `device`.  Idle pooled
+// workspaces are preferred; with none idle and the pool full, the oldest one is
+// waited for (the host is then more than kPoolMax plans ahead of the device) and
+// reused, so steady-state planning allocates nothing.
+ak_status acquire_ws(int device, size_t dev_bytes, size_t host_bytes, Workspace* out) {
+  Workspace w;
+  bool found = false;
+  {
+    std::lock_guard<std::mutex> lk(g_pool_mu);
+    int idle_fit = -1, idle_any = -1, oldest = -1;
+    for (size_t i = 0; i < g_pool.size(); ++i) {
+      Workspace& c = g_pool[i];
+      if (c.device != device) continue;
+      if (oldest < 0) oldest = (int)i;
+      if (c.done && hipEventQuery(c.done) != hipSuccess) continue;
+      if (c.dev_bytes >= dev_bytes && c.host_bytes >= host_bytes) {
+        idle_fit = (int)i;
+        break;
+      }
+      if (idle_any < 0) idle_any = (int)i;
+    }
+    int pick = idle_fit >= 0 ? idle_fit : idle_any;
+    if (pick < 0 && g_pool.size() >= kPoolMax) pick = oldest;
+    if (pick >= 0) {
+      w = g_pool[pick];
+      g_pool.erase(g_pool.begin() + pick);
+      found = true;
+    }
+  }
+  if (found && w.done) (void)hipEventSynchronize(w.done);   // immediate unless host is far ahead
+  w.device = device;
+  ak_status st = size_ws(w, dev_bytes, host_bytes);
+  if (st != AK_OK) {
     release_ws(w);
-    return hip_fail(e, "ak_plan: pinned staging / event");
+    return st;
   }
   *out = w;
   return AK_OK;
 }
 
 void return_ws(Workspace& w) {
-  if (!w.dev) return;
+  if (!w.dev && !w.host) return;
   std::lock_guard<std::mutex> lk(g_pool_mu);
   g_pool.push_back(w);
-  if (g_pool.size() > kPoolMax) {
-    // drop the oldest entry; its event says whether its last use is finished
-    Workspace old = g_pool.front();
-    g_pool.erase(g_pool.begin());
-    if (old.done) (void)hipEventSynchronize(old.done);
-    release_ws(old);
-  }
   w = Workspace{};
 }
 
@@ -567,6 +598,16 @@ extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* s
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(d_off);
   if (e != hipSuccess) return hip_fail(e, "ak_gather_slots");
+  return AK_OK;
+}
+
+extern "C" ak_status ak_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {
+  if (n < 0 || (n % 8) != 0) return fail(AK_ERR_INVALID_ARG, "ak_fp8_to_bf16: n must be a multiple of 8");
+  if (n == 0) return AK_OK;
+  if (!codes || !out || ((uintptr_t)codes & 7u) || ((uintptr_t)out & 15u))
+    return fail(AK_ERR_INVALID_ARG, "ak_fp8_to_bf16: null or misaligned pointer");
+  hipError_t e = launch_fp8_to_bf16(codes, out, n, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ak_fp8_to_bf16");
   return AK_OK;
 }
 

@@ -119,7 +119,25 @@ __global__ __launch_bounds__(256) void gather_slots_kernel(const Req* __restrict
   }
 }
 
+__global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* __restrict__ codes,
+                                                          uint16_t* __restrict__ out, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x2 w = reinterpret_cast<const u32x2*>(codes)[i];
+    reinterpret_cast<u32x4*>(out)[i] = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(w[0], w[1]));
+  }
+}
+
 }  // namespace
+
+hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 <= 0) return hipSuccess;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(fp8_to_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, out, n8);
+  return hipGetLastError();
+}
 
 hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s) {
   const int64_t total = (int64_t)a.N * a.Hkv * (a.D >> 3);

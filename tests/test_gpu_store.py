@@ -109,3 +109,17 @@ def test_store_rejects_bad_arguments():
     with pytest.raises(ak.AkError) as e:
         ak.ak_store_kv(k, k, s64[:3], kc, kc.clone())
     assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH
+
+
+def test_fp8_widening_exhaustive():
+    """The kernels' E4M3 -> bf16 widening on every finite code equals the format
+    definition (oracle decode table), bit for bit."""
+    codes = np.arange(256, dtype=np.uint8)
+    finite = np.isfinite(C.E4M3_VALUES)
+    codes = np.tile(codes[finite], 4)            # 254 finite codes, length a multiple of 8
+    codes = codes[: len(codes) // 8 * 8]
+    got = ak.ak_fp8_to_bf16(torch.from_numpy(codes).cuda())
+    torch.cuda.synchronize()
+    got_bits = got.cpu().view(torch.int16).numpy().view(np.uint16)
+    exp_bits = C.bf16_encode(C.e4m3_decode(codes).astype(np.float32))
+    assert np.array_equal(got_bits, exp_bits)
