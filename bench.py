@@ -198,6 +198,30 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     return res
 
 
+def copy_bandwidth(torch, dev, gib):
+    """Device-to-device copy of `gib` GiB (a plain copy kernel of known size):
+    read + write bytes over the average time of 5 copies, as context for the
+    HBM roofline."""
+    n = int(gib * (1 << 30))
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 5
+    gbs = 2 * n / (ms * 1e-3) / 1e9
+    log(f"[bench] device copy of {gib} GiB: {ms * 1e3:.1f} us -> {gbs:.1f} GB/s (read + write)")
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def cpu_baseline(wl, budget_s=12.0, n_req=16):
@@ -249,6 +273,8 @@ def main():
     ap.add_argument("--also", default="prefill",
                     help="comma list of further workloads: prefill,mixed,longfp8 ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-gib", type=float, default=1.0,
+                    help="size of the device-to-device copy timed as bandwidth context (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -261,6 +287,7 @@ def main():
     from synth import workloads as W
 
     dev = torch.device("cuda:0")
+    copy = copy_bandwidth(torch, dev, args.copy_gib) if args.copy_gib > 0 else None
     dec = measure(ak, torch, dev, W.config(2), args.layers, args.steps, args.warmup)
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
@@ -302,6 +329,7 @@ def main():
             "traffic": None,
         },
         "cpu_baseline": cpu,
+        "copy_GBs": copy,
     }
     for name, r in extra.items():
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),

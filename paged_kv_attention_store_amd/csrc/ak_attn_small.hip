@@ -212,7 +212,10 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
     mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;
     const float m_new = (mb > m_run + kLazy) ? mb : m_run;
     if (__any(m_new != m_run)) {
-      const float alpha = fast_exp2(m_run - m_new);   // 0 when m_run was -inf
+      // rows whose reference stays put keep alpha = 1 (this also covers rows that
+      // have seen no visible key yet: -inf - -inf would be NaN); a row leaving
+      // -inf gets exp2(-inf) = 0
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)

@@ -135,6 +135,12 @@ EDGE = [
     ("fp32_prefill", [1, 70, 3], [40, 100, 200], 16, 8, 2, 64, "f32", "f32", True, (-1, 10)),
     ("fp32_d128", [2, 1], [33, 129], 4, 4, 1, 128, "f32", "f32", True, (-1,)),
     ("multi_row_small", [2, 4, 3], [2000, 1500, 999], 16, 8, 2, 128, "bf16", "bf16", True, (-1, 700)),
+    # regression: a decode-shaped tile whose first query row sees nothing in the
+    # last KV block while the second row does (its running max must stay finite)
+    ("multi_row_tail", [2, 2], [65, 33], 64, 16, 2, 128, "bf16", "bf16", True, (-1, 1)),
+    # regression: a prefill tile where the window start (clamped at 0 for early
+    # rows) makes some rows of a wave see nothing in a block that others see
+    ("window_straddle", [128, 128], [178, 300], 16, 8, 8, 128, "bf16", "bf16", True, (80, 40, 7)),
 ]
 
 
