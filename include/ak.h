@@ -111,7 +111,9 @@ typedef struct {
   float sm_scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim)            */
   int32_t num_cus;       /* compute units to balance for; 0 = ask the device (256
                             in host-only plans)                                    */
-  int32_t max_splits;    /* upper bound on KV splits per (request, KV head); 0 = 64 */
+  int32_t max_splits;    /* bound on KV splits per (request, KV head); 0 = 64.  Exceeded
+                            only when a split would span more than 1024 pages (page
+                            size 1 or 2 with long contexts)                        */
   int32_t min_chunk;     /* smallest KV split in tokens; 0 = library default       */
   int32_t flags;         /* AK_PLAN_HOST_ONLY                                       */
   void* stream;          /* stream for the plan's upload; NULL = default stream     */

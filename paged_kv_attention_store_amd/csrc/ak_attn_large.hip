@@ -16,11 +16,13 @@
 //   * K is staged as 16-byte chunks XOR-swizzled by token (conflict-free MFMA
 //     operand reads); V is staged transposed (d-major, 4-token groups swizzled
 //     by d) so a PV operand is two 8-byte reads;
-//   * S^T (64 tokens x 32 rows) = K Q^T with 32x32x16 bf16 MFMA, Q in registers;
+//   * each 32-token half of a block goes through S^T (32 tokens x 32 rows) =
+//     K Q^T (32x32x16 bf16 MFMA, Q in registers), softmax and PV before the
+//     next half, so one S accumulator is live at a time (no register spills);
 //   * softmax in base 2 with the scale folded into one FMA per score; a row lives
-//     in lanes n and n+32 (one xor-shuffle for its block max); masks are applied
-//     only on blocks that cross a row's causal or window bound;
-//   * the running max is raised only when a block exceeds it by more than 2^8
+//     in lanes n and n+32 (one xor-shuffle for its max); masks are applied only
+//     on tiles that cross a row's causal or window bound;
+//   * the running max is raised only when a tile exceeds it by more than 2^8
 //     (the normalisation is exact for any reference value; this only skips
 //     rescaling O, and probabilities stay below 2^8);
 //   * O^T (D x 32 rows) += V^T P^T, P taken from the S^T registers as produced.
@@ -209,76 +211,72 @@ __global__ __launch_bounds__(256, 2) void attn_large_kernel(AttnArgs a) {
     if (b + 1 < nb) load_block(cur ^ 1);   // lands while this block is computed
 
     if (wave_active) {
-      // ---- S^T = K Q^T: two 32-token tiles
-      f32x16 sacc[2];
+      // two 32-token tiles, each through S^T, softmax and PV before the next
+      // (one S accumulator live at a time)
 #pragma unroll
       for (int T = 0; T < 2; ++T) {
+        // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
+        f32x16 sacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[T][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
         const int t = 32 * T + n32;
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
           const bf16x8 kop =
               *reinterpret_cast<const bf16x8*>(&ks[cur][8 * k_pos<D>(t, 2 * s + hf)]);
-          sacc[T] = mfma32(kop, qop[s], sacc[T]);
+          sacc = mfma32(kop, qop[s], sacc);
         }
-      }
-      // ---- mask (boundary blocks only); element i of tile T is token 32T + 8(i/4) + 4hf + i%4
-      const bool need_mask = (tb < wave_lo_max) | (tb + kKB > wave_hi_min);
-      if (need_mask) {
-#pragma unroll
-        for (int T = 0; T < 2; ++T)
+        // ---- mask (tiles crossing a row bound only); element i is token 32T + 8(i/4) + 4hf + i%4
+        const int tt0 = tb + 32 * T;
+        if ((tt0 < wave_lo_max) | (tt0 + 32 > wave_hi_min)) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int t = tb + 32 * T + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!((t >= row_lo) & (t < row_hi))) sacc[T][i] = -INFINITY;
+            const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
           }
-      }
-      float mb = -INFINITY;
+        }
+        float mb = -INFINITY;
 #pragma unroll
-      for (int T = 0; T < 2; ++T)
+        for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
+        mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;       // tile max in base-2 units
+        // raise the reference max only when the tile exceeds it by kLazy
+        const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+        if (__any(m_new != m_run)) {
+          // rows whose reference stays put keep alpha = 1 (this also covers rows that
+          // have seen no visible key yet: -inf - -inf would be NaN); a row leaving
+          // -inf gets exp2(-inf) = 0
+          const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+          l_run *= alpha;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[T][i]);
-      mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;       // block max in base-2 units
-      // raise the reference max only when the block exceeds it by kLazy
-      const float m_new = (mb > m_run + kLazy) ? mb : m_run;
-      if (__any(m_new != m_run)) {
-        // rows whose reference stays put keep alpha = 1 (this also covers rows that
-        // have seen no visible key yet: -inf - -inf would be NaN); a row leaving
-        // -inf gets exp2(-inf) = 0
-        const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
+          for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int T = 0; T < 2; ++T)
+            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+          m_run = m_new;
+        }
+        const float msub = m_run == -INFINITY ? 0.f : m_run;
+        float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          sacc[T][i] = fast_exp2(__builtin_fmaf(sacc[T][i], c, -msub));
-          psum += sacc[T][i];
+          sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+          psum += sacc[i];
         }
-      l_run += psum;
-      // ---- O^T += V^T P^T over four 16-token k-steps
+        l_run += psum;
+        // ---- O^T += V^T P^T over the tile's two 16-token k-steps
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int T = kk >> 1, i0 = 8 * (kk & 1);
-        u32x4 pw;
+        for (int kh = 0; kh < 2; ++kh) {
+          const int kk = 2 * T + kh, i0 = 8 * kh;
+          u32x4 pw;
 #pragma unroll
-        for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[T][i0 + 2 * h], sacc[T][i0 + 2 * h + 1]);
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+          for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
+          const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const int d = 32 * dt + n32;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + hf)]);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + 2 + hf)]);
-          const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          oacc[dt] = mfma32(vop, pop, oacc[dt]);
+          for (int dt = 0; dt < NDT; ++dt) {
+            const int d = 32 * dt + n32;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + hf)]);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + 2 + hf)]);
+            const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+            oacc[dt] = mfma32(vop, pop, oacc[dt]);
+          }
         }
       }
     }

@@ -9,19 +9,21 @@
 // heads of one KV head share every K/V byte, so they form one tile).
 //
 // gfx950 mapping.  One workgroup (4 waves) per work item; wave w takes the
-// item's 32-token blocks w, w+4, ...  Each wave runs a two-stage register
-// pipeline: while block k is computed, block k+1's K and V rows are in flight
-// into a second register set, and the page ids of block k+2 are in flight too,
-// so every wave keeps two blocks of HBM reads outstanding.  Per block:
-//   S^T (32 tokens x 16 rows) = K (tokens x D) * Q^T   two 16x16x32 bf16 MFMA
-//     tiles per 32 d; K rows go straight from HBM into the MFMA A operand
-//     (each lane loads 32 contiguous bytes of one token row per step pair);
+// item's blocks w, w+4, ... (16 tokens for bf16 rows, 32 for fp8 rows).  The
+// item's page ids are staged once in LDS.  Each wave runs a two-stage register
+// pipeline: block k+1's K and V rows are in flight into a second register set
+// while block k is computed; the loads are unconditional (clamped addresses) so
+// the compiler's memory-counter waits let exactly the next block stay in flight.
+// Per block:
+//   S^T (tokens x 16 rows) = K * Q^T   16x16x32 bf16 MFMA per 16 tokens; K rows
+//     go straight from HBM into the MFMA A operand (each lane loads 16-32
+//     contiguous bytes of one token row per step pair);
 //   online softmax per row in base 2 (the scale carries log2(e)); a row lives in
 //     the 4 lanes l%16 = row, so its max needs two xor-shuffles; the reference
 //     max is raised only when a block exceeds it by more than 2^8;
-//   O^T (D x 16 rows) += V^T * P^T   one 16x16x32 MFMA per 16 d; P stays in the
-//     registers the S^T tile produced it in, V is staged through LDS and read
-//     column-wise.
+//   O^T (D x 16 rows) += V^T * P^T   per 16 d: one 16x16x16 MFMA (16-token
+//     blocks) or 16x16x32 MFMA (32-token blocks); P stays in the registers the
+//     S^T tile produced it in, V is staged through LDS and read column-wise.
 // The d order inside a 32-wide k-step is permuted identically for K and Q
 // (contraction order is free), and the token order inside PV's k-steps follows
 // the S^T register layout identically for P and V.  FP8 rows are widened to
@@ -38,7 +40,6 @@ namespace ak {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kBlk = 32;         // tokens per wave block
 constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
 
 template <int D>
@@ -47,28 +48,42 @@ __device__ __forceinline__ int dmap(int s, int g4) {
   return 64 * (s >> 1) + 16 * g4 + 8 * (s & 1);
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4;
+
+// D(16x16) += A(16x16) * B(16x16), bf16 inputs: lane l holds A[l%16][4*(l/16) .. +4],
+// B[4*(l/16) .. +4][l%16]; D as for the 16x16x32 form.
+__device__ __forceinline__ f32x4 mfma16k16(s16x4 a, s16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
 template <int D, bool FP8>
-struct Blk {
-  static constexpr int NSTEP = D / 32;
-  static constexpr int KL = FP8 ? (NSTEP + 1) / 2 : NSTEP;          // 16-byte K loads per tile
-  static constexpr int CPR = (D * (FP8 ? 1 : 2)) / 16;              // 16-byte chunks per V row
-  static constexpr int TPI = 64 / CPR;                              // V tokens per load instruction
-  static constexpr int VL = kBlk / TPI;                             // 16-byte V loads per lane
-  u32x4 k[2][KL];
-  u32x4 v[VL];
+struct Shape {
+  // bf16 rows stream 16 tokens per wave block (halving the registers a block
+  // needs), fp8 rows 32 tokens
+  static constexpr int BLK = FP8 ? 32 : 16;
+  static constexpr int NT = BLK / 16;                           // S^T tiles per block
+  static constexpr int NSTEP = D / 32;                          // S^T k-steps
+  static constexpr int NDT = D / 16;                            // O^T d-tiles
+  static constexpr int EB = FP8 ? 1 : 2;                        // cache bytes per element
+  static constexpr int KL = FP8 ? (NSTEP + 1) / 2 : NSTEP;      // 16-byte K loads per tile
+  static constexpr int CPR = D * EB / 16;                       // 16-byte chunks per cache row
+  static constexpr int TPI = 64 / CPR;                          // tokens per V load instruction
+  static constexpr int VL = BLK / TPI;                          // V load instructions per block
+  static constexpr int VROW = D + 4;                            // padded row of the V stage
+  static constexpr int STAGE = BLK * VROW;                      // bf16 elements per wave stage
 };
 
 template <int D, bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
-  using B = Blk<D, FP8>;
-  constexpr int NSTEP = D / 32;       // S^T k-steps
-  constexpr int NDT = D / 16;         // O^T d-tiles
-  constexpr int VROW = D + 4;         // bf16 per staged V row (pad: conflict-free column reads)
+  using S = Shape<D, FP8>;
+  constexpr int BLK = S::BLK, NT = S::NT, NSTEP = S::NSTEP, NDT = S::NDT, EB = S::EB;
+  constexpr int KL = S::KL, CPR = S::CPR, TPI = S::TPI, VL = S::VL, VROW = S::VROW;
   constexpr int ORW = D + 4;          // floats per row of the combine buffer
-  constexpr int STAGE_BYTES = kWaves * kBlk * VROW * 2;
+  constexpr int STAGE_BYTES = kWaves * S::STAGE * 2;
   constexpr int COMB_BYTES = (2 * kWaves * 16 + kWaves * 16 * ORW) * 4;
   constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
   __shared__ __align__(16) unsigned char smem[SMEM];
+  __shared__ int32_t s_pages[kSmallMaxPages];
 
   const Item it = a.items[blockIdx.x];
   const Req rq = a.reqs[it.r];
@@ -78,6 +93,19 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   const int g4 = lane >> 4;
   const int G = a.G;
 
+  // ---- the item's page ids, clamped into the pool, staged once in LDS (the
+  // loop then reads them from LDS: no global index load sits between two
+  // blocks' data loads in the in-order memory counter)
+  const int32_t kv_begin = it.kv_begin, kv_end = it.kv_end;
+  const int first_page = kv_begin >> a.log2B;
+  {
+    const int npages = ((kv_end - 1) >> a.log2B) - first_page + 1;   // <= kSmallMaxPages (plan)
+    for (int i = threadIdx.x; i < npages; i += 256) {
+      int64_t pg = a.kv_indices[rq.page_off + first_page + i];
+      s_pages[i] = (int32_t)(pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg));
+    }
+  }
+
   // ---- this lane's query row (column of S^T and O^T)
   const bool rvalid = n16 < it.nrows;
   const int rho = it.row0 + n16;
@@ -85,7 +113,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   const int head = it.hk * G + (rho - jq * G);
   const int64_t qtok = (int64_t)rq.q_off + jq;
   const int qpos = rq.L - rq.n + jq;
-  int row_lo = it.kv_begin, row_hi = it.kv_end;
+  int row_lo = kv_begin, row_hi = kv_end;
   if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
   if (a.causal) row_hi = min(row_hi, qpos + 1);
   if (!rvalid) row_lo = row_hi = 0;
@@ -116,98 +144,98 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.score_scale;
 
-  const int32_t kv_begin = it.kv_begin, kv_end = it.kv_end;
-  const int nblk = (kv_end - kv_begin + kBlk - 1) / kBlk;
+  const int nblk = (kv_end - kv_begin + BLK - 1) / BLK;
   const int nloc = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;   // this wave's blocks
   const int32_t bmask = (1 << a.log2B) - 1;
-  constexpr int EB = FP8 ? 1 : 2;
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * EB;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * EB;
   const int64_t kps = a.k_sp * EB, kbs = a.k_sb * EB, vps = a.v_sp * EB, vbs = a.v_sb * EB;
-  __bf16* vs = reinterpret_cast<__bf16*>(smem) + wave * kBlk * VROW;
+  __bf16* vs = reinterpret_cast<__bf16*>(smem) + wave * S::STAGE;
 
-  // page id of this lane's token (lane & 31) in local block k
-  auto page_for = [&](int k) -> int32_t {
-    const int t = min(kv_begin + (wave + kWaves * k) * kBlk + (lane & 31), kv_end - 1);
-    return (int32_t)kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
+  struct Regs {               // one block's K operands and V rows, as loaded
+    u32x4 k[NT][KL];
+    u32x4 v[VL];
   };
-  // issue the HBM reads of local block k (page ids of its tokens in `pg`)
-  auto load_blk = [&](B& blk, int32_t pg, int k) {
-    const int tb = kv_begin + (wave + kWaves * k) * kBlk;
+
+  // cache row of token t (clamped to the item) -> byte offset of its page/slot
+  auto row_off = [&](int t, int64_t ps, int64_t bs) -> int64_t {
+    t = min(t, kv_end - 1);
+    return (int64_t)s_pages[(t >> a.log2B) - first_page] * ps + (int64_t)(t & bmask) * bs;
+  };
+  // issue the HBM reads of local block k (rows past the item are clamped, so a
+  // prefetch past the last block reads valid memory)
+  auto issue = [&](Regs& rg, int k) {
+    const int tb = kv_begin + (wave + kWaves * k) * BLK;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      const int tt = 16 * T + n16;
-      const int t = min(tb + tt, kv_end - 1);
-      const int64_t page = __shfl(pg, tt, 64);
-      const char* row = kbase + page * kps + (int64_t)(t & bmask) * kbs;
+    for (int T = 0; T < NT; ++T) {
+      const char* row = kbase + row_off(tb + 16 * T + n16, kps, kbs);
 #pragma unroll
-      for (int p = 0; p < B::KL; ++p) {
+      for (int p = 0; p < KL; ++p) {
         const int d0 = FP8 ? 64 * p + 16 * g4 : dmap<D>(p, g4);
-        blk.k[T][p] = *reinterpret_cast<const u32x4*>(row + d0 * EB);
+        rg.k[T][p] = *reinterpret_cast<const u32x4*>(row + d0 * EB);
       }
     }
-    const int cidx = lane % B::CPR;
+    const int cslot = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < B::VL; ++i) {
-      const int tt = i * B::TPI + lane / B::CPR;
-      const int t = min(tb + tt, kv_end - 1);
-      const int64_t page = __shfl(pg, tt, 64);
-      blk.v[i] = *reinterpret_cast<const u32x4*>(vbase + page * vps + (int64_t)(t & bmask) * vbs +
-                                                 cidx * 16);
+    for (int i = 0; i < VL; ++i) {
+      const int r = i * TPI + lane / CPR;
+      rg.v[i] = *reinterpret_cast<const u32x4*>(vbase + row_off(tb + r, vps, vbs) + cslot * 16);
     }
   };
-  // attention over local block k held in `blk`
-  auto compute_blk = [&](const B& blk, int k) {
-    const int tb = kv_begin + (wave + kWaves * k) * kBlk;
-    // ---- V rows into this wave's LDS stage (8-byte pieces: staged rows are 8-byte aligned)
+  // attention over local block k held in `rg`
+  auto compute = [&](const Regs& rg, int k) {
+    const int tb = kv_begin + (wave + kWaves * k) * BLK;
+    // ---- the block's V rows into the wave's stage (bf16; 8-byte pieces, rows are 8-byte aligned)
     {
-      const int cidx = lane % B::CPR;
+      const int cslot = lane % CPR;
 #pragma unroll
-      for (int i = 0; i < B::VL; ++i) {
-        const int tt = i * B::TPI + lane / B::CPR;
-        u32x2* dst = reinterpret_cast<u32x2*>(vs + tt * VROW + cidx * (FP8 ? 16 : 8));
+      for (int i = 0; i < VL; ++i) {
+        const int r = i * TPI + lane / CPR;
+        u32x2* dst = reinterpret_cast<u32x2*>(vs + r * VROW + cslot * (16 / EB));
         if (FP8) {
-          const u32x4 lo = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(blk.v[i][0], blk.v[i][1]));
-          const u32x4 hi = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(blk.v[i][2], blk.v[i][3]));
+          const u32x4 lo = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(rg.v[i][0], rg.v[i][1]));
+          const u32x4 hi = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(rg.v[i][2], rg.v[i][3]));
           dst[0] = u32x2{lo[0], lo[1]};
           dst[1] = u32x2{lo[2], lo[3]};
           dst[2] = u32x2{hi[0], hi[1]};
           dst[3] = u32x2{hi[2], hi[3]};
         } else {
-          dst[0] = u32x2{blk.v[i][0], blk.v[i][1]};
-          dst[1] = u32x2{blk.v[i][2], blk.v[i][3]};
+          dst[0] = u32x2{rg.v[i][0], rg.v[i][1]};
+          dst[1] = u32x2{rg.v[i][2], rg.v[i][3]};
         }
       }
     }
     // ---- S^T = K Q^T
-    f32x4 sacc[2];
+    f32x4 sacc[NT];
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
+    for (int T = 0; T < NT; ++T) {
       sacc[T] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < NSTEP; ++s) {
         bf16x8 kop;
         if (FP8) {
-          const u32x4& w = blk.k[T][s >> 1];
+          const u32x4& w = rg.k[T][s >> 1];
           kop = (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
         } else {
-          kop = __builtin_bit_cast(bf16x8, blk.k[T][s]);
+          kop = __builtin_bit_cast(bf16x8, rg.k[T][s]);
         }
         sacc[T] = mfma16(kop, qop[s], sacc[T]);
       }
     }
     // ---- online softmax (base 2), rows = lane % 16; element i of tile T is token 16T + 4g4 + i
-    if ((tb < wave_lo_max) | (tb + kBlk > wave_hi_min)) {
+    if ((tb < wave_lo_max) | (tb + BLK > wave_hi_min)) {
 #pragma unroll
-      for (int T = 0; T < 2; ++T)
+      for (int T = 0; T < NT; ++T)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = tb + 16 * T + 4 * g4 + i;
           if (!((t >= row_lo) & (t < row_hi))) sacc[T][i] = -INFINITY;
         }
     }
-    float mb = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
-                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    float mb = -INFINITY;
+#pragma unroll
+    for (int T = 0; T < NT; ++T)
+      mb = fmaxf(mb, fmaxf(fmaxf(sacc[T][0], sacc[T][1]), fmaxf(sacc[T][2], sacc[T][3])));
     mb = fmaxf(mb, shfl_xor_f(mb, 16));
     mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;
     const float m_new = (mb > m_run + kLazy) ? mb : m_run;
@@ -224,60 +252,71 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float msub = m_run == -INFINITY ? 0.f : m_run;
-    float p[2][4];
+    float p[NT][4];
 #pragma unroll
-    for (int T = 0; T < 2; ++T)
+    for (int T = 0; T < NT; ++T)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         p[T][i] = fast_exp2(__builtin_fmaf(sacc[T][i], c, -msub));
         l_run += p[T][i];
       }
-    u32x4 pw;
-    pw[0] = pack_bf16x2(p[0][0], p[0][1]);
-    pw[1] = pack_bf16x2(p[0][2], p[0][3]);
-    pw[2] = pack_bf16x2(p[1][0], p[1][1]);
-    pw[3] = pack_bf16x2(p[1][2], p[1][3]);
-    const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-    // the V stage is private to this wave: wait for its LDS writes (and keep the
-    // compiler from moving LDS accesses across this point)
+    // the stage is private to this wave: make its writes visible to all lanes
+    // (and keep the compiler from moving LDS accesses across this point)
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    // ---- O^T += V^T P^T ; k-slot 8*g4 + jj <-> token 16*(jj/4) + 4*g4 + jj%4
     const uint16_t* vsu = reinterpret_cast<const uint16_t*>(vs);
+    if (NT == 2) {
+      // ---- O^T += V^T P^T (16x16x32); k-slot 8*g4 + jj <-> token 16*(jj/4) + 4*g4 + jj%4
+      u32x4 pw;
+      pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+      pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+      pw[2] = pack_bf16x2(p[NT - 1][0], p[NT - 1][1]);
+      pw[3] = pack_bf16x2(p[NT - 1][2], p[NT - 1][3]);
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      const int d = 16 * dt + n16;
-      u32x4 vw;
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = 16 * dt + n16;
+        u32x4 vw;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int jj0 = 2 * h, jj1 = 2 * h + 1;
-        const int t0 = 16 * (jj0 >> 2) + 4 * g4 + (jj0 & 3);
-        const int t1 = 16 * (jj1 >> 2) + 4 * g4 + (jj1 & 3);
-        vw[h] = (uint32_t)vsu[t0 * VROW + d] | ((uint32_t)vsu[t1 * VROW + d] << 16);
+        for (int h = 0; h < 4; ++h) {
+          const int jj0 = 2 * h, jj1 = 2 * h + 1;
+          const int t0 = 16 * (jj0 >> 2) + 4 * g4 + (jj0 & 3);
+          const int t1 = 16 * (jj1 >> 2) + 4 * g4 + (jj1 & 3);
+          vw[h] = (uint32_t)vsu[t0 * VROW + d] | ((uint32_t)vsu[t1 * VROW + d] << 16);
+        }
+        oacc[dt] = mfma16(__builtin_bit_cast(bf16x8, vw), pop, oacc[dt]);
       }
-      oacc[dt] = mfma16(__builtin_bit_cast(bf16x8, vw), pop, oacc[dt]);
+    } else {
+      // ---- O^T += V^T P^T (16x16x16); k-slot 4*g4 + jj <-> token 4*g4 + jj
+      const u32x2 pw{pack_bf16x2(p[0][0], p[0][1]), pack_bf16x2(p[0][2], p[0][3])};
+      const s16x4 pop = __builtin_bit_cast(s16x4, pw);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const int d = 16 * dt + n16;
+        const int t0 = 4 * g4;
+        const u32x2 vw{(uint32_t)vsu[t0 * VROW + d] | ((uint32_t)vsu[(t0 + 1) * VROW + d] << 16),
+                       (uint32_t)vsu[(t0 + 2) * VROW + d] | ((uint32_t)vsu[(t0 + 3) * VROW + d] << 16)};
+        oacc[dt] = mfma16k16(__builtin_bit_cast(s16x4, vw), pop, oacc[dt]);
+      }
     }
-    // the next block's staging writes must not pass this block's reads
+    // the next block's stage writes must not pass this block's reads
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // ---- two-stage pipeline over this wave's blocks (ping-pong register sets)
+  __syncthreads();   // page table staged
+
+  // ---- two-stage register pipeline over this wave's blocks: block k+1's reads
+  // are issued before block k is computed (unconditionally, so the compiler's
+  // memory-counter waits stay exact)
   if (nloc > 0) {
-    B b0, b1;
-    int32_t pg1 = nloc > 1 ? page_for(1) : 0;
-    int32_t pg2 = nloc > 2 ? page_for(2) : 0;
-    load_blk(b0, page_for(0), 0);
-    for (int k = 0; k < nloc; k += 2) {
-      if (k + 1 < nloc) {
-        load_blk(b1, pg1, k + 1);
-        if (k + 3 < nloc) pg1 = page_for(k + 3);
-      }
-      compute_blk(b0, k);
+    Regs ra, rb;
+    issue(ra, 0);
+    for (int k = 0;; k += 2) {
+      issue(rb, k + 1);
+      compute(ra, k);
       if (k + 1 >= nloc) break;
-      if (k + 2 < nloc) {
-        load_blk(b0, pg2, k + 2);
-        if (k + 4 < nloc) pg2 = page_for(k + 4);
-      }
-      compute_blk(b1, k + 1);
+      issue(ra, k + 2);
+      compute(rb, k + 1);
+      if (k + 2 >= nloc) break;
     }
   }
 

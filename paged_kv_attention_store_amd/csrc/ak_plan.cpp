@@ -150,33 +150,44 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
   chunk = std::max<int64_t>(chunk, min_chunk);
 
+  // Units longest first: their parts then come out in (nearly) decreasing size,
+  // so the tail of the grid holds the short items without sorting every item.
+  std::vector<int32_t> order(small.size());
+  for (size_t i = 0; i < small.size(); ++i) order[i] = (int32_t)i;
+  std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    const int32_t lx = small[x].hi - small[x].lo, ly = small[y].hi - small[y].lo;
+    return lx != ly ? lx > ly : x < y;
+  });
+  p->small_items.reserve(small.size() + (size_t)(small_tokens / chunk) + 16);
+
   int64_t prow = 0;
   int64_t split_units = 0;
-  for (const Unit& u : small) {
+  for (int32_t ui : order) {
+    const Unit& u = small[ui];
     const int64_t len = (int64_t)u.hi - u.lo;
     int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, chunk)));
-    if (S <= 1) {
-      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0});
-      continue;
-    }
     // boundaries on a kKvAlign grid anchored below lo
     const int64_t base = (u.lo / kKvAlign) * kKvAlign;
-    const int64_t per = round_up(ceil_div((int64_t)u.hi - base, S), kKvAlign);
-    std::vector<std::pair<int32_t, int32_t>> parts;
-    for (int64_t s = 0;; ++s) {
-      const int64_t a = std::max<int64_t>(u.lo, base + s * per);
-      const int64_t b = std::min<int64_t>(u.hi, base + (s + 1) * per);
-      if (a >= u.hi) break;
-      parts.emplace_back((int32_t)a, (int32_t)b);
+    int64_t per, nparts;
+    for (;;) {
+      per = round_up(ceil_div((int64_t)u.hi - base, S), kKvAlign);
+      nparts = S <= 1 ? 1 : ceil_div((int64_t)u.hi - base, per);
+      // every part must fit a small tile's page table (only binds for tiny pages)
+      const int64_t span = nparts <= 1 ? (((int64_t)u.hi - 1) >> p->log2B) - (u.lo >> p->log2B) + 1
+                                       : (per + B - 1) / B + 1;
+      if (span <= kSmallMaxPages) break;
+      S = std::max<int64_t>(S + 1, ceil_div(S * span, kSmallMaxPages - 1));
     }
-    if (parts.size() == 1) {
+    if (nparts <= 1) {
       p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0});
       continue;
     }
     const int64_t ubase = prow;
-    for (size_t s = 0; s < parts.size(); ++s)
-      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, parts[s].first, parts[s].second,
-                                    (int32_t)(ubase + (int64_t)s * u.rows), 0});
+    for (int64_t s = 0; s < nparts; ++s) {
+      const int32_t a = (int32_t)std::max<int64_t>(u.lo, base + s * per);
+      const int32_t b = (int32_t)std::min<int64_t>(u.hi, base + (s + 1) * per);
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0});
+    }
     const Req& q = p->reqs[u.r];
     for (int32_t rho = 0; rho < u.rows; ++rho) {
       MergeJob m{};
@@ -184,22 +195,24 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       m.head = u.hk * G + rho % G;
       m.pfirst = (int32_t)(ubase + rho);
       m.pstride = u.rows;
-      m.count = (int32_t)parts.size();
+      m.count = (int32_t)nparts;
       p->merges.push_back(m);
     }
-    prow += (int64_t)parts.size() * u.rows;
+    prow += nparts * u.rows;
     ++split_units;
     if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
   }
   p->partial_rows = prow;
   p->split_units = split_units;
 
-  // Longest work first, so the tail of the grid holds the short items.
-  std::stable_sort(p->small_items.begin(), p->small_items.end(), [](const Item& a, const Item& b) {
-    return (a.kv_end - a.kv_begin) > (b.kv_end - b.kv_begin);
-  });
-  std::stable_sort(p->large_items.begin(), p->large_items.end(), [](const Item& a, const Item& b) {
-    return (int64_t)a.nrows * (a.kv_end - a.kv_begin) > (int64_t)b.nrows * (b.kv_end - b.kv_begin);
+  // Large tiles: most work first.
+  std::sort(p->large_items.begin(), p->large_items.end(), [](const Item& a, const Item& b) {
+    const int64_t ca = (int64_t)a.nrows * (a.kv_end - a.kv_begin);
+    const int64_t cb = (int64_t)b.nrows * (b.kv_end - b.kv_begin);
+    if (ca != cb) return ca > cb;
+    if (a.r != b.r) return a.r < b.r;
+    if (a.row0 != b.row0) return a.row0 < b.row0;
+    return a.hk < b.hk;
   });
   return AK_OK;
 }

@@ -307,6 +307,55 @@ struct ak_plan_private : ak_plan_t {
   ak::Workspace ws;
 };
 
+namespace ak {
+namespace {
+
+// Destroyed plan objects are kept (their vectors keep their capacity), so the
+// host side of a new plan reuses warm memory instead of faulting in fresh pages.
+constexpr size_t kPlanCacheMax = 16;
+std::mutex g_plan_mu;
+std::vector<ak_plan_private*> g_plan_cache;
+
+ak_plan_private* new_plan() {
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    if (!g_plan_cache.empty()) {
+      ak_plan_private* p = g_plan_cache.back();
+      g_plan_cache.pop_back();
+      return p;
+    }
+  }
+  return new (std::nothrow) ak_plan_private();
+}
+
+void recycle_plan(ak_plan_private* p) {
+  // reset every field to its default but keep the vectors' storage
+  std::vector<int32_t> kv_lens = std::move(p->kv_lens);
+  std::vector<Req> reqs = std::move(p->reqs);
+  std::vector<Item> small = std::move(p->small_items), large = std::move(p->large_items);
+  std::vector<MergeJob> merges = std::move(p->merges);
+  kv_lens.clear();
+  reqs.clear();
+  small.clear();
+  large.clear();
+  merges.clear();
+  *p = ak_plan_private();
+  p->kv_lens = std::move(kv_lens);
+  p->reqs = std::move(reqs);
+  p->small_items = std::move(small);
+  p->large_items = std::move(large);
+  p->merges = std::move(merges);
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (g_plan_cache.size() < kPlanCacheMax) {
+    g_plan_cache.push_back(p);
+    return;
+  }
+  delete p;
+}
+
+}  // namespace
+}  // namespace ak
+
 extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
                              const int32_t* kv_indices, const int32_t* last_page_len,
                              int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
@@ -315,14 +364,14 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
   if (!plan) return fail(AK_ERR_INVALID_ARG, "ak_plan: null output pointer");
   *plan = nullptr;
   const bool host_only = opts && (opts->flags & AK_PLAN_HOST_ONLY);
-  auto* p = new (std::nothrow) ak_plan_private();
+  auto* p = new_plan();
   if (!p) return fail(AK_ERR_OOM, "ak_plan: out of host memory");
   int dev = 0;
   int cus = opts && opts->num_cus > 0 ? opts->num_cus : 0;
   if (!host_only) {
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) {
-      delete p;
+      recycle_plan(p);
       return hip_fail(e, "ak_plan: hipGetDevice");
     }
     if (cus == 0) cus = device_cus(dev);
@@ -336,14 +385,14 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     st = fail(AK_ERR_OOM, "ak_plan: out of host memory");
   }
   if (st != AK_OK) {
-    delete p;
+    recycle_plan(p);
     return st;
   }
   p->host_only = host_only;
   p->device = dev;
   p->kv_indices = kv_indices;
   if (!host_only && p->num_kv_pages > 0 && !kv_indices) {
-    delete p;
+    recycle_plan(p);
     return fail(AK_ERR_INVALID_ARG, "ak_plan: null kv_indices with a non-empty page table");
   }
   if (!host_only) {
@@ -358,7 +407,7 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (p->d_bytes > 0) {
       st = acquire_ws(dev, p->d_bytes, meta, &p->ws);
       if (st != AK_OK) {
-        delete p;
+        recycle_plan(p);
         return st;
       }
       p->d_buf = p->ws.dev;
@@ -385,7 +434,7 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       if (e != hipSuccess) {
         (void)hipStreamSynchronize(s);
         return_ws(p->ws);
-        delete p;
+        recycle_plan(p);
         return hip_fail(e, "ak_plan: upload");
       }
     }
@@ -398,7 +447,7 @@ extern "C" void ak_plan_destroy(ak_plan_t* plan) {
   if (!plan) return;
   auto* pp = static_cast<ak_plan_private*>(plan);
   return_ws(pp->ws);     // the workspace's event covers its last use
-  delete pp;
+  recycle_plan(pp);
 }
 
 // --------------------------------------------------------------------- run
