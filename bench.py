@@ -164,12 +164,22 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     ak.ak_profile_enable(False)
     prof = ak.ak_profile_read()
     ms_step = (t1 - t0) * 1e3 / steps
+    # host cost of planning alone (the in-loop figure also holds any wait for a
+    # free workspace when the host runs ahead of the GPU)
+    t = time.perf_counter()
+    for _ in range(20):
+        for w in wl.windows:
+            ak.ak_plan(wl.qo_indptr, wl.kv_indptr, None, wl.last_page_len, wl.num_qo_heads,
+                       wl.num_kv_heads, wl.head_dim, wl.page_size, causal=wl.causal, window=w,
+                       host_only=True)
+    plan_host_us = (time.perf_counter() - t) / 20 * 1e6
     wins = [wl.windows[i % len(wl.windows)] for i in range(n_layers)]
     dec_bytes = sum(decode_bytes(wl, w, small_only=True) for w in wins)
     flops = sum(prefill_flops(wl, w, large_only=True) for w in wins)
     step_bytes = sum(decode_bytes(wl, w) for w in wins) + n_layers * store_bytes(wl)
     res = dict(wl=wl, ms_step=ms_step, gbs=step_bytes / (ms_step * 1e-3) / 1e9, prof=prof,
                info=ak.ak_plan_info(plans[0]), plan_us=plan_s / steps * 1e6,
+               plan_host_us=plan_host_us,
                step_bytes=step_bytes, layers=n_layers)
     n, ms = prof["attn_small"]
     if n and dec_bytes:
@@ -187,7 +197,7 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     if n:
         res["merge_avg_us"] = ms / n * 1e3
     msg = (f"[bench] {wl.name}: {ms_step:.3f} ms/step, step-level {res['gbs']:.1f} GB/s; "
-           f"plan {res['plan_us']:.1f} us; ")
+           f"plan {res['plan_us']:.1f} us (host only {res['plan_host_us']:.1f} us); ")
     if "small_gbs" in res:
         msg += f"attn_small {res['small_avg_ms'] * 1e3:.1f} us -> {res['small_gbs']:.1f} GB/s; "
     if "large_tflops" in res:
@@ -316,6 +326,7 @@ def main():
             "kv_tokens": int(wl.kv_lens.sum()),
             "bytes_per_step": dec["step_bytes"],
             "plan_us": round(dec["plan_us"], 1),
+            "plan_host_us": round(dec["plan_host_us"], 1),
             "plan": dec["info"],
         },
         "roofline": {
@@ -333,7 +344,8 @@ def main():
     }
     for name, r in extra.items():
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
-             "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1)}
+             "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1),
+             "plan_host_us": round(r["plan_host_us"], 1)}
         if "small_gbs" in r:
             e["decode"] = {"kernel": "attn_small", "achieved": round(r["small_gbs"], 1),
                            "unit": "GB/s", "peak": HBM_PEAK_GBS,

@@ -1,4 +1,4 @@
-// Large-tile paged attention: 128 query rows of one (request, KV head) -- the
+// Large-tile paged attention: 256 query rows of one (request, KV head) -- the
 // extend/prefill shape, where the rows are (query token, head of the group)
 // pairs packed token-major so GQA heads share every K/V tile.
 //
@@ -7,12 +7,15 @@
 // come from" (causal bit and window_left, never a materialised mask); the GQA
 // head-group fusion figure of "Why metadata is built once per step".
 //
-// gfx950 mapping.  One workgroup of 4 waves per 128-row tile, wave w owning rows
-// 32w .. 32w+31; two workgroups share a CU (<= 256 registers per lane, 66 KB of
-// LDS each).  The KV range is walked in 64-token blocks with a software pipeline:
-//   * block i+1's K and V rows are loaded into registers while block i is
-//     computed from LDS, then written into the other LDS buffer (one barrier per
-//     block); the page ids of block i+2 are fetched one iteration earlier still;
+// gfx950 mapping.  One workgroup of 8 waves per 256-row tile, wave w owning rows
+// 32w .. 32w+31 (one workgroup per CU, <= 256 registers per lane, 66 KB of LDS).
+// The KV range is walked in 64-token blocks with a software pipeline:
+//   * block i+1's K rows (waves 4-7) and V rows (waves 0-3) are loaded into
+//     registers while block i is computed from LDS, then written into the other
+//     LDS buffer (one barrier per block); the page ids of block i+2 are fetched
+//     one iteration earlier still.  256 rows per tile give each loaded K/V byte
+//     twice the MFMA work of a 128-row tile, and twice the compute to hide the
+//     next block's gather behind;
 //   * K is staged as 16-byte chunks XOR-swizzled by token (conflict-free MFMA
 //     operand reads); V is staged transposed (d-major, 4-token groups swizzled
 //     by d) so a PV operand is two 8-byte reads;
@@ -49,19 +52,20 @@ __device__ __forceinline__ int vt_pos(int d, int tg) {
 }
 
 template <int D, bool FP8>
-__global__ __launch_bounds__(256, 2) void attn_large_kernel(AttnArgs a) {
+__global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
   constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
   constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
   constexpr int CPR = D / 8;                  // 16-byte bf16 chunks per row
   constexpr int SCPR = FP8 ? CPR / 2 : CPR;   // 16-byte source chunks per row
-  constexpr int KLD = kKB * SCPR / 256;       // K source chunks per thread per block
+  constexpr int KLD = kKB * SCPR / 256;       // K source chunks per K-loader thread per block
   constexpr int VPAIRS = (kKB / 4) * CPR;     // (4-token group, 8-column chunk) pairs
-  static_assert(KLD >= 1 && VPAIRS <= 256, "tile shape");
+  static_assert(KLD >= 1 && KLD <= 4 && VPAIRS <= 256, "tile shape");
   __shared__ __align__(16) __bf16 ks[2][kKB * D];
   __shared__ __align__(16) __bf16 vt[2][D * kKB];
   __shared__ int64_t s_koff[2][kKB], s_voff[2][kKB];
 
   const Item it = a.items[blockIdx.x];
+  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
   const Req rq = a.reqs[it.r];
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
@@ -126,55 +130,59 @@ __global__ __launch_bounds__(256, 2) void attn_large_kernel(AttnArgs a) {
     s_voff[buf][lane] = (page * a.v_sp + slot * a.v_sb) * ebytes;
   };
 
-  // prefetch registers: K source chunks, V rows of one (group, chunk) pair
-  u32x4 kreg[KLD];
-  u32x4 vreg[4];
-  const int vu = tid & 15, vc = tid >> 4;   // V pair of this thread (valid if tid < VPAIRS)
+  // prefetch registers: waves 4-7 hold K source chunks, waves 0-3 the V rows of
+  // one (4-token group, 8-column chunk) pair
+  u32x4 pre[4];
+  const bool k_loader = wave >= 4;
+  const int lt = tid & 255;                  // index among the 256 loaders of a kind
+  const int vu = lt & 15, vc = lt >> 4;      // V pair (valid if lt < VPAIRS)
   auto load_block = [&](int buf) {
+    if (k_loader) {
 #pragma unroll
-    for (int k = 0; k < KLD; ++k) {
-      const int q = tid + 256 * k;
-      const int t = q / SCPR, cc = q % SCPR;
-      kreg[k] = *reinterpret_cast<const u32x4*>(kbase + s_koff[buf][t] + cc * 16);
-    }
-    if (tid < VPAIRS) {
+      for (int k = 0; k < KLD; ++k) {
+        const int q = lt + 256 * k;
+        const int t = q / SCPR, cc = q % SCPR;
+        pre[k] = *reinterpret_cast<const u32x4*>(kbase + s_koff[buf][t] + cc * 16);
+      }
+    } else if (lt < VPAIRS) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const char* src = vbase + s_voff[buf][4 * vu + j];
         if (FP8) {
           const u32x2 w = *reinterpret_cast<const u32x2*>(src + vc * 8);
-          vreg[j] = u32x4{w[0], w[1], 0u, 0u};
+          pre[j] = u32x4{w[0], w[1], 0u, 0u};
         } else {
-          vreg[j] = *reinterpret_cast<const u32x4*>(src + vc * 16);
+          pre[j] = *reinterpret_cast<const u32x4*>(src + vc * 16);
         }
       }
     }
   };
   auto store_block = [&](int buf) {
+    if (k_loader) {
 #pragma unroll
-    for (int k = 0; k < KLD; ++k) {
-      const int q = tid + 256 * k;
-      const int t = q / SCPR, cc = q % SCPR;
-      if (FP8) {
-        *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc)]) =
-            e4m3x8_to_bf16x8(kreg[k][0], kreg[k][1]);
-        *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc + 1)]) =
-            e4m3x8_to_bf16x8(kreg[k][2], kreg[k][3]);
-      } else {
-        *reinterpret_cast<u32x4*>(&ks[buf][8 * k_pos<D>(t, cc)]) = kreg[k];
+      for (int k = 0; k < KLD; ++k) {
+        const int q = lt + 256 * k;
+        const int t = q / SCPR, cc = q % SCPR;
+        if (FP8) {
+          *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc)]) =
+              e4m3x8_to_bf16x8(pre[k][0], pre[k][1]);
+          *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc + 1)]) =
+              e4m3x8_to_bf16x8(pre[k][2], pre[k][3]);
+        } else {
+          *reinterpret_cast<u32x4*>(&ks[buf][8 * k_pos<D>(t, cc)]) = pre[k];
+        }
       }
-    }
-    if (tid < VPAIRS) {
+    } else if (lt < VPAIRS) {
       uint32_t e[4][4];   // e[token][dword]: bf16 pairs of columns 8vc .. 8vc+7
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (FP8) {
-          const u32x4 b = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(vreg[j][0], vreg[j][1]));
+          const u32x4 b = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(pre[j][0], pre[j][1]));
 #pragma unroll
           for (int k = 0; k < 4; ++k) e[j][k] = b[k];
         } else {
 #pragma unroll
-          for (int k = 0; k < 4; ++k) e[j][k] = vreg[j][k];
+          for (int k = 0; k < 4; ++k) e[j][k] = pre[j][k];
         }
       }
 #pragma unroll
@@ -329,13 +337,13 @@ hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<128, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_large_kernel<128, false>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<64, false>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_large_kernel<64, false>), grid, dim3(512), 0, s, a);
   } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<128, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_large_kernel<128, true>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<64, true>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((attn_large_kernel<64, true>), grid, dim3(512), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

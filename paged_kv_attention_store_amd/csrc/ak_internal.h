@@ -13,7 +13,7 @@ namespace ak {
 // of the request (position L - n + j), query head hk * G + g.
 
 constexpr int kSmallRows = 16;    // rows of a small (decode-shaped) tile
-constexpr int kLargeRows = 128;   // rows of a large (prefill-shaped) tile
+constexpr int kLargeRows = 256;   // rows of a large (prefill-shaped) tile
 constexpr int kKvAlign = 64;      // KV split boundaries are multiples of this
 constexpr int kSmallMaxPages = 1024;  // pages a small-tile item may span (its LDS page table)
 
