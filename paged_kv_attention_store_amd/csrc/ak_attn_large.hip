@@ -331,15 +331,279 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 caches: K and V tiles are copied HBM -> LDS by the load-to-LDS path
+// (global_load_lds, 16 bytes per lane), so staging costs neither registers nor
+// VALU work.  Each lane fetches the source chunk that belongs at its LDS slot,
+// which applies the swizzle on the gather side:
+//   * K rows: chunk c of token t sits at slot c ^ kswz(t) (conflict-free 16-byte
+//     operand reads for S^T = K Q^T);
+//   * V rows stay token-major (chunk c at slot c ^ vswz(t)); the V^T operand of
+//     O^T += V^T P^T comes from two transposing 8-byte reads (ds_read_b64_tr_b16),
+//     each giving a lane one column of V over 4 consecutive tokens.
+// The two LDS buffer pairs are distinct variables and the block loop is unrolled
+// by two, so the compiler can tell that reads of the current buffer never alias
+// the copy in flight into the other one (no memory-counter wait between them).
+
+template <int D>
+__device__ __forceinline__ int vswz(int t) {
+  return D == 128 ? 4 * (t & 3) : 4 * ((t >> 1) & 1);
+}
+
+template <int D>
+__global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
+  constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
+  constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int TILE = kKB * D;               // bf16 elements of one K or V tile
+  constexpr int NI = kKB * CPR / (64 * 8);    // load-to-LDS instructions per wave per tile
+  static_assert(NI >= 1 && NI * 64 * 8 == kKB * CPR, "tile shape");
+  __shared__ __align__(16) __bf16 k0s[TILE];
+  __shared__ __align__(16) __bf16 v0s[TILE];
+  __shared__ __align__(16) __bf16 k1s[TILE];
+  __shared__ __align__(16) __bf16 v1s[TILE];
+  __shared__ int64_t s_koff[2][kKB], s_voff[2][kKB];
+
+  const Item it = a.items[blockIdx.x];
+  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
+  const Req rq = a.reqs[it.r];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n32 = lane & 31;
+  const int hf = lane >> 5;
+  const int G = a.G;
+
+  // ---- this lane's row
+  const int rl = wave * 32 + n32;
+  const bool rvalid = rl < it.nrows;
+  const int rho = it.row0 + rl;
+  const int jq = rho / G;
+  const int head = it.hk * G + (rho - jq * G);
+  const int64_t qtok = (int64_t)rq.q_off + jq;
+  const int qpos = rq.L - rq.n + jq;
+  int row_lo = it.kv_begin, row_hi = it.kv_end;
+  if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
+  if (a.causal) row_hi = min(row_hi, qpos + 1);
+  if (!rvalid) row_lo = row_hi = 0;
+  // tiles entirely inside [wave_lo_max, wave_hi_min) need no mask
+  int wave_lo_max = row_lo, wave_hi_min = row_hi;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, k, 64));
+    wave_hi_min = min(wave_hi_min, __shfl_xor(wave_hi_min, k, 64));
+  }
+  const bool wave_active = (wave * 32) < it.nrows;
+
+  bf16x8 qop[NS];
+  {
+    const __bf16* qp = static_cast<const __bf16*>(a.q) + qtok * a.q_st + (int64_t)head * a.q_sh;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qop[s] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hf)
+                      : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
+  }
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.score_scale;
+
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * 2;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * 2;
+  const int32_t bmask = (1 << a.log2B) - 1;
+  const int nb = (it.kv_end - it.kv_begin + kKB - 1) / kKB;
+
+  // page id of this lane's token in block b (wave 0 only), as stored; it is clamped
+  // into the pool where it is used, so the load stays in flight until then
+  auto page_raw = [&](int b) -> int32_t {
+    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
+    return a.kv_indices[rq.page_off + (t >> a.log2B)];
+  };
+  auto put_offsets = [&](int b, int32_t raw, int buf) {
+    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
+    const int64_t page = raw < 0 ? 0 : (raw >= a.num_pages ? a.num_pages - 1 : (int64_t)raw);
+    const int64_t slot = t & bmask;
+    s_koff[buf][lane] = (page * a.k_sp + slot * a.k_sb) * 2;
+    s_voff[buf][lane] = (page * a.v_sp + slot * a.v_sb) * 2;
+  };
+
+  // ---- copy one block's K and V rows into (kd, vd): this wave's NI x 64 chunks of each
+  auto issue_copy = [&](auto& kd, auto& vd, int buf) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
+      const int q = q0 + lane;
+      const int t = q / CPR, j = q % CPR;
+      const char* gk = kbase + s_koff[buf][t] + 16 * (j ^ (D == 128 ? (t & 15) : ((t >> 1) & 7)));
+      const char* gv = vbase + s_voff[buf][t] + 16 * (j ^ vswz<D>(t));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
+                                       (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gv),
+                                       (__attribute__((address_space(3))) void*)(&vd[8 * q0]),
+                                       16, 0, 0);
+    }
+  };
+
+  // V^T operand reads.  The P^T operand of k-step kk holds, in lane half hf, the
+  // probabilities of tokens 16kk + 4hf + 0..3 and 16kk + 8 + 4hf + 0..3 (the order
+  // the S^T accumulator produces them in), so V^T must list the same tokens.  Lane
+  // l of a 16-lane group g = l >> 4 reads 8 bytes of token row 4hf + (l & 15) / 4
+  // (+8 for the second read, +16kk for k-step kk) at column 32dt + 16(g & 1) +
+  // 4(l & 3); the transposing read hands lane l column 32dt + (l & 31) over the
+  // 4 tokens read by its group.
+  const int vr_tok = 4 * hf + ((lane & 15) >> 2);             // token within a 16-token k-step
+  const int vr_sw = vswz<D>(vr_tok);                           // token & 3 is fixed per lane
+  const int vr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-column d-tile
+  auto v_elem = [&](int kk, int dt, int second) -> int {
+    const int tok = 16 * kk + vr_tok + 8 * second;
+    const int col = 32 * dt + vr_col;
+    return tok * D + 8 * ((col >> 3) ^ vr_sw) + (col & 7);
+  };
+
+  auto compute = [&](auto& kc, auto& vc, int tb) {
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+      // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
+      f32x16 sacc;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+      const int t = 32 * T + n32;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&kc[8 * k_pos<D>(t, 2 * s + hf)]);
+        sacc = mfma32(kop, qop[s], sacc);
+      }
+      // ---- mask (tiles crossing a row bound only); element i is token 32T + 8(i/4) + 4hf + i%4
+      const int tt0 = tb + 32 * T;
+      if ((tt0 < wave_lo_max) | (tt0 + 32 > wave_hi_min)) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
+        }
+      }
+      float mb = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
+      mb = halves_max(mb) * c;                     // tile max in base-2 units
+      const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+      if (__any(m_new != m_run)) {
+        // alpha = 1 where the reference stays (also rows with no visible key yet)
+        const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float msub = m_run == -INFINITY ? 0.f : m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+        psum += sacc[i];
+      }
+      l_run += psum;
+      // ---- O^T += V^T P^T over the tile's two 16-token k-steps
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int kk = 2 * T + kh, i0 = 8 * kh;
+        u32x4 pw;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
+        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
+          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+          const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+          oacc[dt] = mfma32(vop, pop, oacc[dt]);
+        }
+      }
+    }
+  };
+
+  // ---- one block: start the copy of block b+1 and the page-id loads of block b+2,
+  // compute block b, then store block b+2's offsets (block b's are no longer read)
+  auto step = [&](int b, auto& kc, auto& vc, auto& kn, auto& vn) {
+    if (b + 1 < nb) issue_copy(kn, vn, (b + 1) & 1);
+    const bool next_offsets = wave == 0 && b + 2 < nb;
+    const int32_t raw = next_offsets ? page_raw(b + 2) : 0;
+    if (wave_active) compute(kc, vc, it.kv_begin + b * kKB);
+    if (next_offsets) put_offsets(b + 2, raw, b & 1);
+    __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
+    __syncthreads();
+  };
+
+  // ---- prologue: offsets of blocks 0 and 1, block 0 copied
+  if (wave == 0) {
+    put_offsets(0, page_raw(0), 0);
+    if (nb > 1) put_offsets(1, page_raw(1), 1);
+  }
+  __syncthreads();
+  issue_copy(k0s, v0s, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  for (int b = 0; b < nb; b += 2) {
+    step(b, k0s, v0s, k1s, v1s);
+    if (b + 1 >= nb) break;
+    step(b + 1, k1s, v1s, k0s, v0s);
+  }
+
+  // ---- finalise: O^T element i of tile dt is column d = 32dt + 8(i/4) + 4hf + i%4
+  const float l_tot = halves_sum(l_run);
+  if (!rvalid) return;
+  const bool any = l_tot > 0.f;
+  const float inv = any ? a.v_scale / l_tot : 0.f;
+  const float lse2 = any ? m_run + log2f(l_tot) : -INFINITY;
+  if (it.pbase < 0) {
+    uint16_t* op = static_cast<uint16_t*>(a.out) + qtok * a.o_st + (int64_t)head * a.o_sh;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hf;
+        const u32x2 w{pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                      pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
+        *reinterpret_cast<u32x2*>(op + d0) = w;
+      }
+    if (a.lse && hf == 0) a.lse[qtok * a.l_st + (int64_t)head * a.l_sh] = lse2 * kLn2;
+  } else {
+    const int64_t prow = (int64_t)it.pbase + rl;
+    float* pp = a.part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hf;
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                  oacc[dt][4 * g + 3] * inv};
+      }
+    if (hf == 0) a.part_lse[prow] = lse2;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<128, false>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma_kernel<128>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<64, false>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma_kernel<64>), grid, dim3(512), 0, s, a);
   } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
     hipLaunchKernelGGL((attn_large_kernel<128, true>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
