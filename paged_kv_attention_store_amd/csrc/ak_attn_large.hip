@@ -39,6 +39,7 @@ namespace {
 
 constexpr int kKB = 64;          // tokens per KV block
 constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
+constexpr int kDmaKB = 128;      // tokens per KV block of the bf16 (load-to-LDS) kernel
 
 template <int D>
 __device__ __forceinline__ int k_pos(int t, int c) {
@@ -344,25 +345,39 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
 // The two LDS buffer pairs are distinct variables and the block loop is unrolled
 // by two, so the compiler can tell that reads of the current buffer never alias
 // the copy in flight into the other one (no memory-counter wait between them).
+//
+// A block of KB tokens is NT = KB/32 tiles.  Blocks that lie inside every row
+// bound of the wave take the fast path: no masks, and the S^T MFMAs of tile T+1
+// are issued before the softmax of tile T, so the matrix core works on the next
+// tile while the vector ALU exponentiates this one (the two waves of a SIMD,
+// kept in step by the block barrier, would otherwise both wait on the same
+// unit).  Other blocks go tile by tile with masks, skipping tiles no row of the
+// wave can see.
 
+template <int D>
+__device__ __forceinline__ int kswz(int t) {
+  return D == 128 ? (t & 15) : ((t >> 1) & 7);
+}
 template <int D>
 __device__ __forceinline__ int vswz(int t) {
   return D == 128 ? 4 * (t & 3) : 4 * ((t >> 1) & 1);
 }
 
-template <int D>
+template <int D, int KB>
 __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
   constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
   constexpr int CPR = D / 8;                  // 16-byte chunks per row
-  constexpr int TILE = kKB * D;               // bf16 elements of one K or V tile
-  constexpr int NI = kKB * CPR / (64 * 8);    // load-to-LDS instructions per wave per tile
-  static_assert(NI >= 1 && NI * 64 * 8 == kKB * CPR, "tile shape");
+  constexpr int NT = KB / 32;                 // 32-token tiles per block
+  constexpr int TILE = KB * D;                // bf16 elements of one K or V block
+  constexpr int NI = KB * CPR / (64 * 8);     // load-to-LDS instructions per wave per block
+  constexpr int OPL = KB / 64;                // block tokens per lane of wave 0 (offsets)
+  static_assert(NI >= 1 && NI * 64 * 8 == KB * CPR && OPL * 64 == KB, "tile shape");
   __shared__ __align__(16) __bf16 k0s[TILE];
   __shared__ __align__(16) __bf16 v0s[TILE];
   __shared__ __align__(16) __bf16 k1s[TILE];
   __shared__ __align__(16) __bf16 v1s[TILE];
-  __shared__ int64_t s_koff[2][kKB], s_voff[2][kKB];
+  __shared__ int64_t s_koff[2][KB], s_voff[2][KB];
 
   const Item it = a.items[blockIdx.x];
   if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
@@ -385,13 +400,17 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   int row_lo = it.kv_begin, row_hi = it.kv_end;
   if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
   if (a.causal) row_hi = min(row_hi, qpos + 1);
-  if (!rvalid) row_lo = row_hi = 0;
-  // tiles entirely inside [wave_lo_max, wave_hi_min) need no mask
-  int wave_lo_max = row_lo, wave_hi_min = row_hi;
+  if (!rvalid) row_lo = row_hi = INT_MIN;       // sees nothing; neutral in the bounds below
+  // [lo_max, hi_min): every valid row of the wave sees it (no mask needed);
+  // outside [lo_min, hi_max): no row of the wave sees it (nothing to compute)
+  int lo_max = rvalid ? row_lo : INT_MIN, hi_min = rvalid ? row_hi : INT_MAX;
+  int lo_min = rvalid ? row_lo : INT_MAX, hi_max = rvalid ? row_hi : INT_MIN;
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) {
-    wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, k, 64));
-    wave_hi_min = min(wave_hi_min, __shfl_xor(wave_hi_min, k, 64));
+    lo_max = max(lo_max, __shfl_xor(lo_max, k, 64));
+    hi_min = min(hi_min, __shfl_xor(hi_min, k, 64));
+    lo_min = min(lo_min, __shfl_xor(lo_min, k, 64));
+    hi_max = max(hi_max, __shfl_xor(hi_max, k, 64));
   }
   const bool wave_active = (wave * 32) < it.nrows;
 
@@ -415,20 +434,27 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * 2;
   const int32_t bmask = (1 << a.log2B) - 1;
-  const int nb = (it.kv_end - it.kv_begin + kKB - 1) / kKB;
+  const int nb = (it.kv_end - it.kv_begin + KB - 1) / KB;
 
-  // page id of this lane's token in block b (wave 0 only), as stored; it is clamped
-  // into the pool where it is used, so the load stays in flight until then
-  auto page_raw = [&](int b) -> int32_t {
-    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
-    return a.kv_indices[rq.page_off + (t >> a.log2B)];
+  // page ids of this lane's tokens in block b (wave 0 only), as stored; they are
+  // clamped into the pool where they are used, so the loads stay in flight until then
+  auto page_raw = [&](int b, int32_t (&raw)[OPL]) {
+#pragma unroll
+    for (int r = 0; r < OPL; ++r) {
+      const int t = min(it.kv_begin + b * KB + lane + 64 * r, it.kv_end - 1);
+      raw[r] = a.kv_indices[rq.page_off + (t >> a.log2B)];
+    }
   };
-  auto put_offsets = [&](int b, int32_t raw, int buf) {
-    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
-    const int64_t page = raw < 0 ? 0 : (raw >= a.num_pages ? a.num_pages - 1 : (int64_t)raw);
-    const int64_t slot = t & bmask;
-    s_koff[buf][lane] = (page * a.k_sp + slot * a.k_sb) * 2;
-    s_voff[buf][lane] = (page * a.v_sp + slot * a.v_sb) * 2;
+  auto put_offsets = [&](int b, const int32_t (&raw)[OPL], int buf) {
+#pragma unroll
+    for (int r = 0; r < OPL; ++r) {
+      const int t = min(it.kv_begin + b * KB + lane + 64 * r, it.kv_end - 1);
+      const int64_t page =
+          raw[r] < 0 ? 0 : (raw[r] >= a.num_pages ? a.num_pages - 1 : (int64_t)raw[r]);
+      const int64_t slot = t & bmask;
+      s_koff[buf][lane + 64 * r] = (page * a.k_sp + slot * a.k_sb) * 2;
+      s_voff[buf][lane + 64 * r] = (page * a.v_sp + slot * a.v_sb) * 2;
+    }
   };
 
   // ---- copy one block's K and V rows into (kd, vd): this wave's NI x 64 chunks of each
@@ -438,7 +464,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
       const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
       const int q = q0 + lane;
       const int t = q / CPR, j = q % CPR;
-      const char* gk = kbase + s_koff[buf][t] + 16 * (j ^ (D == 128 ? (t & 15) : ((t >> 1) & 7)));
+      const char* gk = kbase + s_koff[buf][t] + 16 * (j ^ kswz<D>(t));
       const char* gv = vbase + s_voff[buf][t] + 16 * (j ^ vswz<D>(t));
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                        (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
@@ -465,70 +491,91 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     return tok * D + 8 * ((col >> 3) ^ vr_sw) + (col & 7);
   };
 
-  auto compute = [&](auto& kc, auto& vc, int tb) {
+  // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
+  auto s_tile = [&](auto& kc, int T) -> f32x16 {
+    f32x16 sacc;
 #pragma unroll
-    for (int T = 0; T < 2; ++T) {
-      // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
-      f32x16 sacc;
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+    const int t = 32 * T + n32;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-      const int t = 32 * T + n32;
+    for (int s = 0; s < NS; ++s) {
+      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&kc[8 * (t * CPR + ((2 * s + hf) ^ kswz<D>(t)))]);
+      sacc = mfma32(kop, qop[s], sacc);
+    }
+    return sacc;
+  };
+
+  // ---- online softmax of one tile and O^T += V^T P^T over its two 16-token k-steps
+  auto softmax_pv = [&](auto& vc, f32x16 sacc, int T) {
+    float mb = -INFINITY;
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&kc[8 * k_pos<D>(t, 2 * s + hf)]);
-        sacc = mfma32(kop, qop[s], sacc);
+    for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
+    mb = halves_max(mb) * c;                     // tile max in base-2 units
+    // raise the reference max only when the tile exceeds it by kLazy
+    const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+    if (__any(m_new != m_run)) {
+      // alpha = 1 where the reference stays (also rows with no visible key yet:
+      // -inf - -inf would be NaN); a row leaving -inf gets exp2(-inf) = 0
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      m_run = m_new;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+      psum += sacc[i];
+    }
+    l_run += psum;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kk = 2 * T + kh, i0 = 8 * kh;
+      u32x4 pw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
+      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
+        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+        const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+        oacc[dt] = mfma32(vop, pop, oacc[dt]);
       }
-      // ---- mask (tiles crossing a row bound only); element i is token 32T + 8(i/4) + 4hf + i%4
-      const int tt0 = tb + 32 * T;
-      if ((tt0 < wave_lo_max) | (tt0 + 32 > wave_hi_min)) {
+    }
+  };
+
+  auto compute = [&](auto& kc, auto& vc, int tb) {
+    if (tb >= lo_max && tb + KB <= hi_min) {
+      // fast path: no masks; S^T of tile T+1 in flight during the softmax of tile T
+      f32x16 sa = s_tile(kc, 0);
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        f32x16 sb;
+        if (T + 1 < NT) sb = s_tile(kc, T + 1);
+        softmax_pv(vc, sa, T);
+        if (T + 1 < NT) sa = sb;
+      }
+    } else {
+      for (int T = 0; T < NT; ++T) {
+        const int tt0 = tb + 32 * T;
+        if ((tt0 >= hi_max) | (tt0 + 32 <= lo_min)) continue;   // no row of the wave sees it
+        f32x16 sacc = s_tile(kc, T);
+        // element i is token tt0 + 8(i/4) + 4hf + i%4
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
           if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
         }
-      }
-      float mb = -INFINITY;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
-      mb = halves_max(mb) * c;                     // tile max in base-2 units
-      const float m_new = (mb > m_run + kLazy) ? mb : m_run;
-      if (__any(m_new != m_run)) {
-        // alpha = 1 where the reference stays (also rows with no visible key yet)
-        const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-        m_run = m_new;
-      }
-      const float msub = m_run == -INFINITY ? 0.f : m_run;
-      float psum = 0.f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
-        psum += sacc[i];
-      }
-      l_run += psum;
-      // ---- O^T += V^T P^T over the tile's two 16-token k-steps
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int kk = 2 * T + kh, i0 = 8 * kh;
-        u32x4 pw;
-#pragma unroll
-        for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
-        const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          typedef short v4s __attribute__((ext_vector_type(4)));
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
-          const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-          const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-          oacc[dt] = mfma32(vop, pop, oacc[dt]);
-        }
+        softmax_pv(vc, sacc, T);
       }
     }
   };
@@ -538,8 +585,9 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   auto step = [&](int b, auto& kc, auto& vc, auto& kn, auto& vn) {
     if (b + 1 < nb) issue_copy(kn, vn, (b + 1) & 1);
     const bool next_offsets = wave == 0 && b + 2 < nb;
-    const int32_t raw = next_offsets ? page_raw(b + 2) : 0;
-    if (wave_active) compute(kc, vc, it.kv_begin + b * kKB);
+    int32_t raw[OPL];
+    if (next_offsets) page_raw(b + 2, raw);
+    if (wave_active) compute(kc, vc, it.kv_begin + b * KB);
     if (next_offsets) put_offsets(b + 2, raw, b & 1);
     __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
     __syncthreads();
@@ -547,8 +595,13 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 
   // ---- prologue: offsets of blocks 0 and 1, block 0 copied
   if (wave == 0) {
-    put_offsets(0, page_raw(0), 0);
-    if (nb > 1) put_offsets(1, page_raw(1), 1);
+    int32_t raw[OPL];
+    page_raw(0, raw);
+    put_offsets(0, raw, 0);
+    if (nb > 1) {
+      page_raw(1, raw);
+      put_offsets(1, raw, 1);
+    }
   }
   __syncthreads();
   issue_copy(k0s, v0s, 0);
@@ -601,9 +654,9 @@ hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_dma_kernel<128>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma_kernel<128, kDmaKB>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_dma_kernel<64>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma_kernel<64, kDmaKB>), grid, dim3(512), 0, s, a);
   } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
     hipLaunchKernelGGL((attn_large_kernel<128, true>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
