@@ -491,28 +491,44 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     return tok * D + 8 * ((col >> 3) ^ vr_sw) + (col & 7);
   };
 
-  // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
-  auto s_tile = [&](auto& kc, int T) -> f32x16 {
+  // ---- tile pieces.  Tile T of a block is block tokens 32T .. 32T+31; S^T element
+  // i of a lane is token 32T + 8(i/4) + 4hf + i%4.
+  auto read_k = [&](auto& kc, int T, bf16x8 (&kop)[NS]) {
+    const int t = 32 * T + n32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kop[s] = *reinterpret_cast<const bf16x8*>(&kc[8 * (t * CPR + ((2 * s + hf) ^ kswz<D>(t)))]);
+  };
+  auto s_mfma = [&](const bf16x8 (&kop)[NS]) -> f32x16 {
     f32x16 sacc;
 #pragma unroll
     for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-    const int t = 32 * T + n32;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      const bf16x8 kop = *reinterpret_cast<const bf16x8*>(&kc[8 * (t * CPR + ((2 * s + hf) ^ kswz<D>(t)))]);
-      sacc = mfma32(kop, qop[s], sacc);
-    }
+    for (int s = 0; s < NS; ++s) sacc = mfma32(kop[s], qop[s], sacc);
     return sacc;
   };
-
-  // ---- online softmax of one tile and O^T += V^T P^T over its two 16-token k-steps
-  auto softmax_pv = [&](auto& vc, f32x16 sacc, int T) {
+  auto read_v = [&](auto& vc, int kk, bf16x8 (&vop)[NDT]) {   // k-step kk of the block
+    typedef short v4s __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      vop[dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+  };
+  // tile max (base-2 units); the reference max is raised (rescaling O and l) only
+  // when a tile exceeds it by kLazy
+  auto tile_max = [&](const f32x16& sacc) -> float {
     float mb = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
-    mb = halves_max(mb) * c;                     // tile max in base-2 units
-    // raise the reference max only when the tile exceeds it by kLazy
-    const float m_new = (mb > m_run + kLazy) ? mb : m_run;
+    mb = halves_max(mb) * c;
+    return (mb > m_run + kLazy) ? mb : m_run;
+  };
+  auto raise_max = [&](float m_new) {
     if (__any(m_new != m_run)) {
       // alpha = 1 where the reference stays (also rows with no visible key yet:
       // -inf - -inf would be NaN); a row leaving -inf gets exp2(-inf) = 0
@@ -524,58 +540,79 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
         for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
       m_run = m_new;
     }
+  };
+  // probabilities against the current reference max, packed as the P^T operands
+  // of the tile's two 16-token k-steps; their sum goes into l
+  auto exp_pack = [&](const f32x16& sacc, bf16x8 (&pop)[2]) {
     const float msub = m_run == -INFINITY ? 0.f : m_run;
+    float p[16];
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
-      psum += sacc[i];
+      p[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+      psum += p[i];
     }
     l_run += psum;
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
-      const int kk = 2 * T + kh, i0 = 8 * kh;
       u32x4 pw;
 #pragma unroll
-      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
-      const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        typedef short v4s __attribute__((ext_vector_type(4)));
-        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
-        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
-        const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-        const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
-        oacc[dt] = mfma32(vop, pop, oacc[dt]);
-      }
+      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(p[8 * kh + 2 * h], p[8 * kh + 2 * h + 1]);
+      pop[kh] = __builtin_bit_cast(bf16x8, pw);
     }
+  };
+  auto o_mfma = [&](const bf16x8 (&vop)[NDT], const bf16x8& pop) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(vop[dt], pop, oacc[dt]);
   };
 
   auto compute = [&](auto& kc, auto& vc, int tb) {
+    bf16x8 kop[NS];
+    bf16x8 vop[NDT];
+    bf16x8 pop[2];
     if (tb >= lo_max && tb + KB <= hi_min) {
-      // fast path: no masks; S^T of tile T+1 in flight during the softmax of tile T
-      f32x16 sa = s_tile(kc, 0);
+      // Fast path (no masks), software-pipelined over the block's tiles: while the
+      // probabilities of tile T are formed, the S^T MFMAs of tile T+1 run and the
+      // K operands of tile T+2 and the V operands of tile T are in flight.
+      read_k(kc, 0, kop);
+      f32x16 sa = s_mfma(kop);
+      if (NT > 1) read_k(kc, 1, kop);
+      raise_max(tile_max(sa));
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
+        read_v(vc, 2 * T, vop);
         f32x16 sb;
-        if (T + 1 < NT) sb = s_tile(kc, T + 1);
-        softmax_pv(vc, sa, T);
-        if (T + 1 < NT) sa = sb;
+        if (T + 1 < NT) {
+          sb = s_mfma(kop);
+          if (T + 2 < NT) read_k(kc, T + 2, kop);
+        }
+        exp_pack(sa, pop);
+        o_mfma(vop, pop[0]);
+        read_v(vc, 2 * T + 1, vop);
+        const float m_next = T + 1 < NT ? tile_max(sb) : 0.f;
+        o_mfma(vop, pop[1]);
+        if (T + 1 < NT) {
+          raise_max(m_next);
+          sa = sb;
+        }
       }
     } else {
       for (int T = 0; T < NT; ++T) {
         const int tt0 = tb + 32 * T;
         if ((tt0 >= hi_max) | (tt0 + 32 <= lo_min)) continue;   // no row of the wave sees it
-        f32x16 sacc = s_tile(kc, T);
-        // element i is token tt0 + 8(i/4) + 4hf + i%4
+        read_k(kc, T, kop);
+        f32x16 sacc = s_mfma(kop);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
           if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
         }
-        softmax_pv(vc, sacc, T);
+        raise_max(tile_max(sacc));
+        exp_pack(sacc, pop);
+        read_v(vc, 2 * T, vop);
+        o_mfma(vop, pop[0]);
+        read_v(vc, 2 * T + 1, vop);
+        o_mfma(vop, pop[1]);
       }
     }
   };
