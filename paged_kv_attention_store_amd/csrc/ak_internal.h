@@ -16,6 +16,11 @@ constexpr int kSmallRows = 16;    // rows of a small (decode-shaped) tile
 constexpr int kLargeRows = 256;   // rows of a large (prefill-shaped) tile
 constexpr int kKvAlign = 64;      // KV split boundaries are multiples of this
 constexpr int kSmallMaxPages = 1024;  // pages a small-tile item may span (its LDS page table)
+constexpr int kLargeTile = 32;    // KV tokens per tile of the large-tile cost model
+constexpr int kBlockTiles = 4;    // tiles per KV block of the large-tile kernel (split boundary)
+constexpr int kSegCost = 3;       // start-up cost of a large-tile segment, in tiles
+constexpr int kMinPartTiles = 8;  // smallest KV part a large tile job is split into, in tiles
+constexpr double kTileBytes = 4.0e6;  // bytes the whole GPU streams in one large-tile time
 
 struct Item {          // one workgroup's work; 32 bytes
   int32_t r;           // request

@@ -115,11 +115,12 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     lo = window >= 0 ? (int32_t)std::max<int64_t>(0, pa - window) : 0;
   };
 
-  // ---- small units (<= 16 rows) with their split partition
+  // ---- small units (<= 16 rows) with their split partition; large tile jobs
   struct Unit {
     int32_t r, hk, rows, lo, hi;
   };
   std::vector<Unit> small;
+  std::vector<Item> jobs;   // large tiles, ordered by (request, KV head, first row)
   int64_t small_tokens = 0;
   p->small_items.clear();
   p->large_items.clear();
@@ -134,13 +135,13 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       for (int32_t hk = 0; hk < Hkv; ++hk) small.push_back(Unit{r, hk, (int32_t)rows, lo, hi});
       small_tokens += (int64_t)(hi - lo) * Hkv;
     } else {
-      for (int64_t row0 = 0; row0 < rows; row0 += kLargeRows) {
-        const int64_t nr = std::min<int64_t>(kLargeRows, rows - row0);
-        int32_t lo, hi;
-        kv_range(q, row0, row0 + nr, lo, hi);
-        for (int32_t hk = 0; hk < Hkv; ++hk)
-          p->large_items.push_back(Item{r, hk, (int32_t)row0, (int32_t)nr, lo, hi, -1, 1});
-      }
+      for (int32_t hk = 0; hk < Hkv; ++hk)
+        for (int64_t row0 = 0; row0 < rows; row0 += kLargeRows) {
+          const int64_t nr = std::min<int64_t>(kLargeRows, rows - row0);
+          int32_t lo, hi;
+          kv_range(q, row0, row0 + nr, lo, hi);
+          jobs.push_back(Item{r, hk, (int32_t)row0, (int32_t)nr, lo, hi, -1, 1});
+        }
     }
   }
 
@@ -202,18 +203,109 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     ++split_units;
     if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
   }
+  // ---- large tiles: one workgroup per segment, launched longest first so the
+  // dispatcher's earliest-free-CU order approximates longest-processing-time
+  // scheduling.  The cost of a segment is its 32-token KV tiles plus a fixed
+  // start-up cost.  A job longer than an even share of the work over the compute
+  // units (at least two minimal parts) would alone set the makespan: it is split
+  // along its KV range into parts of about that share, on block boundaries,
+  // merged like split small units -- but only when the makespan gain beats the
+  // estimated cost of the extra partial traffic.
+  if (!jobs.empty()) {
+    auto tiles = [](int64_t lo, int64_t hi) { return ceil_div(hi - lo, kLargeTile); };
+    const size_t nj = jobs.size();
+    int64_t total = 0, longest = 0;
+    for (const Item& j : jobs) {
+      const int64_t c = tiles(j.kv_begin, j.kv_end) + kSegCost;
+      total += c;
+      longest = std::max(longest, c);
+    }
+    const int64_t share = std::max<int64_t>(ceil_div(total, p->num_cus), 2 * kMinPartTiles + kSegCost);
+    std::vector<int32_t> nparts(nj, 1);
+    if (longest > share) {
+      int64_t longest_part = share;
+      double split_bytes = 0.0;
+      for (size_t i = 0; i < nj; ++i) {
+        const int64_t t = tiles(jobs[i].kv_begin, jobs[i].kv_end);
+        if (t + kSegCost <= share) continue;
+        const int64_t k = std::min<int64_t>(ceil_div(t, share - kSegCost), max_splits);
+        if (k < 2) continue;
+        nparts[i] = (int32_t)k;
+        const int64_t per = round_up(ceil_div(t, k), kBlockTiles);
+        longest_part = std::max(longest_part, per + kSegCost);
+        // each part writes an fp32 partial row (+ lse) that the merge reads back,
+        // and the merge writes the output row
+        split_bytes += (double)jobs[i].nrows * ((double)k * 2.0 * (D * 4 + 4) + D * 2);
+      }
+      const double gain = (double)(longest - longest_part);
+      if (gain <= 2.0 * split_bytes / kTileBytes) std::fill(nparts.begin(), nparts.end(), 1);
+    }
+    struct Seg {
+      int32_t job, lo, hi;
+      int64_t cost;
+    };
+    std::vector<Seg> segs;
+    segs.reserve(nj * 2);
+    for (size_t i = 0; i < nj; ++i) {
+      const Item& j = jobs[i];
+      if (nparts[i] <= 1) {
+        segs.push_back(Seg{(int32_t)i, j.kv_begin, j.kv_end, tiles(j.kv_begin, j.kv_end) + kSegCost});
+        continue;
+      }
+      const int64_t t = tiles(j.kv_begin, j.kv_end);
+      const int64_t per = round_up(ceil_div(t, nparts[i]), kBlockTiles) * kLargeTile;
+      int64_t parts = 0;
+      for (int64_t lo = j.kv_begin; lo < j.kv_end; lo += per) {
+        const int64_t hi = std::min<int64_t>(j.kv_end, lo + per);
+        segs.push_back(Seg{(int32_t)i, (int32_t)lo, (int32_t)hi, tiles(lo, hi) + kSegCost});
+        ++parts;
+      }
+      nparts[i] = (int32_t)parts;
+    }
+    // partial rows and merge jobs for split jobs (parts of a job are consecutive)
+    std::vector<int32_t> pbase_of(nj, -1);
+    for (size_t i = 0; i < nj; ++i) {
+      if (nparts[i] <= 1) continue;
+      const Item& j = jobs[i];
+      pbase_of[i] = (int32_t)prow;
+      const Req& q = p->reqs[j.r];
+      for (int32_t rl = 0; rl < j.nrows; ++rl) {
+        const int32_t rho = j.row0 + rl;
+        MergeJob m{};
+        m.token = q.q_off + rho / G;
+        m.head = j.hk * G + rho % G;
+        m.pfirst = (int32_t)(prow + rl);
+        m.pstride = j.nrows;
+        m.count = nparts[i];
+        p->merges.push_back(m);
+      }
+      prow += (int64_t)nparts[i] * j.nrows;
+      ++split_units;
+      if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
+    }
+    p->large_items.reserve(segs.size());
+    int32_t prev = -1, part = 0;
+    for (const Seg& g : segs) {
+      part = g.job == prev ? part + 1 : 0;
+      prev = g.job;
+      Item it = jobs[(size_t)g.job];
+      it.kv_begin = g.lo;
+      it.kv_end = g.hi;
+      it.pbase = pbase_of[(size_t)g.job] < 0 ? -1 : pbase_of[(size_t)g.job] + part * it.nrows;
+      p->large_items.push_back(it);
+    }
+    // longest first; ties in layout order
+    std::vector<int32_t> order(segs.size());
+    for (size_t k = 0; k < segs.size(); ++k) order[k] = (int32_t)k;
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t x, int32_t y) { return segs[(size_t)x].cost > segs[(size_t)y].cost; });
+    std::vector<Item> sorted;
+    sorted.reserve(order.size());
+    for (int32_t k : order) sorted.push_back(p->large_items[(size_t)k]);
+    p->large_items.swap(sorted);
+  }
   p->partial_rows = prow;
   p->split_units = split_units;
-
-  // Large tiles: most work first.
-  std::sort(p->large_items.begin(), p->large_items.end(), [](const Item& a, const Item& b) {
-    const int64_t ca = (int64_t)a.nrows * (a.kv_end - a.kv_begin);
-    const int64_t cb = (int64_t)b.nrows * (b.kv_end - b.kv_begin);
-    if (ca != cb) return ca > cb;
-    if (a.r != b.r) return a.r < b.r;
-    if (a.row0 != b.row0) return a.row0 < b.row0;
-    return a.hk < b.hk;
-  });
   return AK_OK;
 }
 

@@ -192,3 +192,57 @@ def test_over_planning_trap_is_a_hard_check():
     # (shape mismatch) -- here: the plan records its head geometry
     p = host_plan([0, 1], [0, 1], [3], hq=8, hkv=2)
     assert p.num_qo_heads == 8
+
+
+# ------------------------------------------------------- large-tile order
+
+def _large(p):
+    items, _ = ak.ak_plan_export(p)
+    info = ak.ak_plan_info(p)
+    return items[info["small_items"]:], info
+
+
+def _cost(large):
+    return np.ceil((large[:, 5] - large[:, 4]) / 32.0)
+
+
+def test_large_tiles_longest_first_without_splits():
+    # many jobs against 256 compute units: no job exceeds the per-unit share, so
+    # nothing is split; the dispatch order is longest KV range first
+    wl = W.config(3)
+    p = host_plan(wl.qo_indptr, wl.kv_indptr, wl.last_page_len, hq=wl.num_qo_heads,
+                  hkv=wl.num_kv_heads, B=wl.page_size, causal=True, window=-1, num_cus=256)
+    large, info = _large(p)
+    assert len(large) > 256 and np.all(large[:, 6] == -1) and info["merge_jobs"] == 0
+    c = _cost(large)
+    assert np.all(np.diff(c) <= 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_large_split_of_few_long_jobs(seed):
+    # few long jobs on many compute units: the longest are split along KV; the
+    # cover stays exact and every split row gets one merge job over its parts
+    rng = np.random.default_rng(100 + seed)
+    R = int(rng.integers(1, 4))
+    Ls = rng.integers(3000, 9000, size=R)
+    ns = np.array([int(rng.integers(17, 300)) for _ in Ls])
+    B = 16
+    pages = -(-Ls // B)
+    kv = np.concatenate([[0], np.cumsum(pages)])
+    qo = np.concatenate([[0], np.cumsum(ns)])
+    last = Ls - (pages - 1) * B
+    P = int(rng.choice([16, 64, 256]))
+    p, _ = check_coverage(qo, kv, last, B, 8, 2, True, -1, num_cus=P)
+    large, info = _large(p)
+    c = _cost(large)
+    assert np.all(np.diff(c) <= 0)
+    split = large[large[:, 6] >= 0]
+    assert len(split) > 0
+    # parts of one job share (request, head, rows) and tile its KV range
+    keys = {tuple(x) for x in split[:, :4].tolist()}
+    n_merge = 0
+    for key in keys:
+        parts = split[np.all(split[:, :4] == np.array(key), axis=1)]
+        assert len(parts) >= 2
+        n_merge += key[3]
+    assert info["small_items"] == 0 and n_merge == info["merge_jobs"]
