@@ -35,6 +35,43 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn HBM GB/s (% peak); prefill attn TFLOP/s (% MFMA peak)"
+
+# Measured HBM traffic of the decode kernel (rocprofv3 FETCH_SIZE / WRITE_SIZE,
+# scaled by the copy-kernel calibration) is kept with its profile summary, tagged
+# with a hash of the sources the kernel is built from; it is reported only while
+# those sources are unchanged.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_small_llama8b_decode_bf16.traffic.txt")
+DECODE_KERNEL_SOURCES = [
+    "paged_kv_attention_store_amd/csrc/ak_attn_small.hip",
+    "paged_kv_attention_store_amd/csrc/ak_device.h",
+    "paged_kv_attention_store_amd/csrc/ak_launch.h",
+    "paged_kv_attention_store_amd/csrc/ak_internal.h",
+    "paged_kv_attention_store_amd/build.py",
+]
+
+
+def decode_kernel_sha() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in DECODE_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per decode-kernel launch from the committed counter summary, or
+    None when there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line)
+    except OSError:
+        return None
+    kv = {k.strip(): v.strip() for k, v in kv.items()}
+    if kv.get("sources_sha256") != decode_kernel_sha():
+        return None
+    return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 EB = {"f32": 4, "bf16": 2, "fp8": 1}
@@ -184,6 +221,7 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     n, ms = prof["attn_small"]
     if n and dec_bytes:
         res["small_avg_ms"] = ms / n
+        res["small_bytes_per_launch"] = int(round(dec_bytes / n_layers))
         res["small_gbs"] = dec_bytes * steps / (ms * 1e-3) / 1e9
     n, ms = prof["attn_large"]
     if n and flops:
@@ -302,8 +340,9 @@ def main():
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
         fac, nl = WORKLOADS[name]
-        extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps // 2), 2)
+        extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
+    traffic = measured_traffic()
     wl = dec["wl"]
     line = {
         "metric": METRIC,
@@ -337,7 +376,8 @@ def main():
             "unit": "GB/s",
             "frac": round(dec["small_gbs"] / HBM_PEAK_GBS, 4),
             "avg_launch_us": round(dec["small_avg_ms"] * 1e3, 2),
-            "traffic": None,
+            "algorithmic_bytes_per_launch": dec["small_bytes_per_launch"],
+            "traffic": traffic,
         },
         "cpu_baseline": cpu,
         "copy_GBs": copy,
