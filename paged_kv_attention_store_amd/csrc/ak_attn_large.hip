@@ -371,13 +371,11 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   constexpr int NT = KB / 32;                 // 32-token tiles per block
   constexpr int TILE = KB * D;                // bf16 elements of one K or V block
   constexpr int NI = KB * CPR / (64 * 8);     // load-to-LDS instructions per wave per block
-  constexpr int OPL = KB / 64;                // block tokens per lane of wave 0 (offsets)
-  static_assert(NI >= 1 && NI * 64 * 8 == KB * CPR && OPL * 64 == KB, "tile shape");
+  static_assert(NI >= 1 && NI * 64 * 8 == KB * CPR, "tile shape");
   __shared__ __align__(16) __bf16 k0s[TILE];
   __shared__ __align__(16) __bf16 v0s[TILE];
   __shared__ __align__(16) __bf16 k1s[TILE];
   __shared__ __align__(16) __bf16 v1s[TILE];
-  __shared__ int64_t s_koff[2][KB], s_voff[2][KB];
 
   const Item it = a.items[blockIdx.x];
   if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
@@ -436,36 +434,28 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   const int32_t bmask = (1 << a.log2B) - 1;
   const int nb = (it.kv_end - it.kv_begin + KB - 1) / KB;
 
-  // page ids of this lane's tokens in block b (wave 0 only), as stored; they are
-  // clamped into the pool where they are used, so the loads stay in flight until then
-  auto page_raw = [&](int b, int32_t (&raw)[OPL]) {
-#pragma unroll
-    for (int r = 0; r < OPL; ++r) {
-      const int t = min(it.kv_begin + b * KB + lane + 64 * r, it.kv_end - 1);
-      raw[r] = a.kv_indices[rq.page_off + (t >> a.log2B)];
-    }
+  // The copy of a block is NI load-to-LDS instructions per wave for K and NI for V;
+  // lane l of instruction i carries chunk q = (wave*NI + i)*64 + l of the block,
+  // i.e. block token q / CPR.  Each wave loads the page ids of its own tokens one
+  // block ahead of the copy (kept as stored; clamped into the pool when used), so
+  // the addresses need no shared table and no LDS round trip.
+  auto copy_token = [&](int b, int i) {
+    return min(it.kv_begin + b * KB + ((wave * NI + i) * 64 + lane) / CPR, it.kv_end - 1);
   };
-  auto put_offsets = [&](int b, const int32_t (&raw)[OPL], int buf) {
+  auto load_pages = [&](int b, int32_t (&raw)[NI]) {
 #pragma unroll
-    for (int r = 0; r < OPL; ++r) {
-      const int t = min(it.kv_begin + b * KB + lane + 64 * r, it.kv_end - 1);
-      const int64_t page =
-          raw[r] < 0 ? 0 : (raw[r] >= a.num_pages ? a.num_pages - 1 : (int64_t)raw[r]);
-      const int64_t slot = t & bmask;
-      s_koff[buf][lane + 64 * r] = (page * a.k_sp + slot * a.k_sb) * 2;
-      s_voff[buf][lane + 64 * r] = (page * a.v_sp + slot * a.v_sb) * 2;
-    }
+    for (int i = 0; i < NI; ++i) raw[i] = a.kv_indices[rq.page_off + (copy_token(b, i) >> a.log2B)];
   };
-
-  // ---- copy one block's K and V rows into (kd, vd): this wave's NI x 64 chunks of each
-  auto issue_copy = [&](auto& kd, auto& vd, int buf) {
+  auto issue_copy = [&](auto& kd, auto& vd, int b, const int32_t (&raw)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
       const int q = q0 + lane;
       const int t = q / CPR, j = q % CPR;
-      const char* gk = kbase + s_koff[buf][t] + 16 * (j ^ kswz<D>(t));
-      const char* gv = vbase + s_voff[buf][t] + 16 * (j ^ vswz<D>(t));
+      const int64_t page = raw[i] < 0 ? 0 : (raw[i] >= a.num_pages ? a.num_pages - 1 : (int64_t)raw[i]);
+      const int64_t slot = copy_token(b, i) & bmask;
+      const char* gk = kbase + (page * a.k_sp + slot * a.k_sb) * 2 + 16 * (j ^ kswz<D>(t));
+      const char* gv = vbase + (page * a.v_sp + slot * a.v_sb) * 2 + 16 * (j ^ vswz<D>(t));
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                        (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
                                        16, 0, 0);
@@ -617,31 +607,21 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     }
   };
 
-  // ---- one block: start the copy of block b+1 and the page-id loads of block b+2,
-  // compute block b, then store block b+2's offsets (block b's are no longer read)
+  // ---- one block: start the copy of block b+1 (page ids loaded during block b-1)
+  // and the page-id loads of block b+2, then compute block b
+  int32_t raw[NI];
   auto step = [&](int b, auto& kc, auto& vc, auto& kn, auto& vn) {
-    if (b + 1 < nb) issue_copy(kn, vn, (b + 1) & 1);
-    const bool next_offsets = wave == 0 && b + 2 < nb;
-    int32_t raw[OPL];
-    if (next_offsets) page_raw(b + 2, raw);
+    if (b + 1 < nb) issue_copy(kn, vn, b + 1, raw);
+    if (b + 2 < nb) load_pages(b + 2, raw);
     if (wave_active) compute(kc, vc, it.kv_begin + b * KB);
-    if (next_offsets) put_offsets(b + 2, raw, b & 1);
     __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
     __syncthreads();
   };
 
-  // ---- prologue: offsets of blocks 0 and 1, block 0 copied
-  if (wave == 0) {
-    int32_t raw[OPL];
-    page_raw(0, raw);
-    put_offsets(0, raw, 0);
-    if (nb > 1) {
-      page_raw(1, raw);
-      put_offsets(1, raw, 1);
-    }
-  }
-  __syncthreads();
-  issue_copy(k0s, v0s, 0);
+  // ---- prologue: block 0 copied, page ids of block 1 loaded
+  load_pages(0, raw);
+  issue_copy(k0s, v0s, 0, raw);
+  if (nb > 1) load_pages(1, raw);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
