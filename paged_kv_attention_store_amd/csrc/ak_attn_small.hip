@@ -10,10 +10,11 @@
 //
 // gfx950 mapping.  One workgroup (4 waves) per work item; wave w takes the
 // item's blocks w, w+4, ... (16 tokens for bf16 rows, 32 for fp8 rows).  The
-// item's page ids are staged once in LDS.  Each wave runs a two-stage register
-// pipeline: block k+1's K and V rows are in flight into a second register set
-// while block k is computed; the loads are unconditional (clamped addresses) so
-// the compiler's memory-counter waits let exactly the next block stay in flight.
+// item's page ids are staged once in LDS.  Each wave runs a register pipeline:
+// the K and V rows of the next block (bf16, D = 128) or next two blocks (fp8
+// rows, D = 64) are in flight into spare register sets while block k is
+// computed; the loads are unconditional (clamped addresses) so the compiler's
+// memory-counter waits keep them in flight.
 // Per block:
 //   S^T (tokens x 16 rows) = K * Q^T   16x16x32 bf16 MFMA per 16 tokens; K rows
 //     go straight from HBM into the MFMA A operand (each lane loads 16-32
@@ -304,19 +305,37 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 
   __syncthreads();   // page table staged
 
-  // ---- two-stage register pipeline over this wave's blocks: block k+1's reads
-  // are issued before block k is computed (unconditionally, so the compiler's
-  // memory-counter waits stay exact)
+  // ---- register pipeline over this wave's blocks: the reads of the next one
+  // (bf16 rows, D = 128) or two (otherwise) blocks are in flight while block k is
+  // computed.  Reads are issued unconditionally, so the compiler's memory-counter
+  // waits stay exact: each compute waits only for its own block.  (A third
+  // register set does not fit beside bf16 D = 128 operands without spills.)
   if (nloc > 0) {
-    Regs ra, rb;
+    constexpr bool kThree = FP8 || D == 64;
+    Regs ra, rb, rc;
     issue(ra, 0);
-    for (int k = 0;; k += 2) {
-      issue(rb, k + 1);
-      compute(ra, k);
-      if (k + 1 >= nloc) break;
-      issue(ra, k + 2);
-      compute(rb, k + 1);
-      if (k + 2 >= nloc) break;
+    if (kThree) {
+      issue(rb, 1);
+      for (int k = 0;; k += 3) {
+        issue(rc, k + 2);
+        compute(ra, k);
+        if (k + 1 >= nloc) break;
+        issue(ra, k + 3);
+        compute(rb, k + 1);
+        if (k + 2 >= nloc) break;
+        issue(rb, k + 4);
+        compute(rc, k + 2);
+        if (k + 3 >= nloc) break;
+      }
+    } else {
+      for (int k = 0;; k += 2) {
+        issue(rb, k + 1);
+        compute(ra, k);
+        if (k + 1 >= nloc) break;
+        issue(ra, k + 2);
+        compute(rb, k + 1);
+        if (k + 2 >= nloc) break;
+      }
     }
   }
 
