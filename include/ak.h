@@ -138,7 +138,9 @@ typedef struct {
  *   last_page_len  host int32 [batch_size]        (copied); in [1, page_size]
  *                  for a request with pages, ignored for one without.
  *   causal         1: key t is visible to a query at position p iff t <= p;
- *                  0: all keys are visible.
+ *                  0: all keys are visible (then n_r may exceed L_r, and a
+ *                  request without pages yields the empty state: out 0,
+ *                  lse -inf -- the prefix segment of a two-segment extend).
  *   window         -1: none; w >= 0 (causal only): keys t >= p - w stay visible,
  *                  i.e. w + 1 keys including the query's own position.
  *   opts           may be NULL.
@@ -152,8 +154,8 @@ typedef struct {
  * num_kv_heads with a group of 1, 2, 4, 8 or 16; head_dim 64 or 128; page_size
  * a power of two in [1, 256].  Errors: AK_ERR_INVALID_ARG, AK_ERR_UNSUPPORTED,
  * AK_ERR_BAD_INDPTR (qo/kv indptr not starting at 0 or decreasing),
- * AK_ERR_BAD_LENGTHS (last_page_len outside [1, page_size], n_r > L_r, queries
- * on a request without pages), AK_ERR_OOM, AK_ERR_HIP.  batch_size = 0 or no
+ * AK_ERR_BAD_LENGTHS (last_page_len outside [1, page_size]; with causal = 1,
+ * n_r > L_r, including queries on a request without pages), AK_ERR_OOM, AK_ERR_HIP.  batch_size = 0 or no
  * query rows gives a valid empty plan. */
 ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                   const int32_t* last_page_len, int32_t batch_size, int32_t num_qo_heads,
@@ -203,6 +205,30 @@ ak_status ak_run(const ak_plan_t* plan, const ak_tensor* q, const ak_tensor* k_c
 /* Thread-local text of the last error (empty string if none).  Owned by the
  * library; valid until the next ak_* call on the same thread. */
 const char* ak_last_error(void);
+
+/* ak_merge_states -- combine two attention states computed over disjoint key
+ * sets of the same queries ("SGLang attention backend", "The two forms of
+ * extend": the prefix/new-token split of an extend step; the shared-prefix
+ * cascade of "vLLM attention backend").  For every (token i, head h):
+ *   m   = max(lse_a, lse_b),  w_x = exp(lse_x - m),
+ *   out = (w_a * o_a + w_b * o_b) / (w_a + w_b),   lse = m + ln(w_a + w_b),
+ * where a state with lse = -inf (no visible key) weighs 0; if both are -inf the
+ * output row is 0 and lse is -inf.
+ *
+ *   o_a, o_b   [T, H, D]  F32 or BF16 (both the dtype of out), D contiguous,
+ *              rows 16-byte aligned; each is normalised (an ak_run output).
+ *   lse_a,
+ *   lse_b      [T, H]     F32, natural log (as ak_run writes it).
+ *   out        [T, H, D]  F32 or BF16; may be the same tensor as o_a or o_b
+ *              (each row is read before it is written).
+ *   lse_out    [T, H]     F32 or NULL; may alias lse_a or lse_b.
+ *
+ * D must be 64 or 128.  Arithmetic in fp32.  Errors: AK_ERR_INVALID_ARG (null
+ * tensor or data), AK_ERR_SHAPE_MISMATCH (shapes disagree), AK_ERR_UNSUPPORTED
+ * (dtype, D, layout), AK_ERR_HIP.  T = 0 or H = 0 launches nothing. */
+ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak_tensor* o_b,
+                          const ak_tensor* lse_b, ak_tensor* out, ak_tensor* lse_out,
+                          void* stream);
 
 /* ak_plan_info -- host-side summary of a plan (any plan, host-only included).
  * Writes up to 8 int64 values into `info` (caller-owned host array):

@@ -11,6 +11,7 @@ Entry points (same names as the C ABI):
     ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads,
             num_kv_heads, head_dim, page_size, causal=True, window=-1, ...) -> Plan
     ak_run(plan, q, k_cache, v_cache, out=None, lse=None, k_scale=1.0, v_scale=1.0)
+    ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None)
     ak_plan_destroy, ak_plan_info, ak_plan_export, ak_gather_slots,
     ak_profile_enable, ak_profile_read, ak_last_error, ak_version
 """
@@ -43,6 +44,7 @@ AK_PLAN_HOST_ONLY = 1
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
+            "ak_merge_states",
             "ak_profile_read", "ak_version", "ak_fp8_to_bf16"]
 
 
@@ -86,6 +88,8 @@ def _load():
     lib.ak_plan_info.restype = ctypes.c_int
     lib.ak_plan_export.argtypes = [ctypes.c_void_p, i32p, ctypes.c_int64, P(ctypes.c_int64), i32p]
     lib.ak_plan_export.restype = ctypes.c_int
+    lib.ak_merge_states.argtypes = [P(AkTensor)] * 6 + [ctypes.c_void_p]
+    lib.ak_merge_states.restype = ctypes.c_int
     lib.ak_gather_slots.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.ak_gather_slots.restype = ctypes.c_int
     lib.ak_profile_enable.argtypes = [ctypes.c_int32]
@@ -247,6 +251,24 @@ def ak_run(plan: Plan, q, k_cache, v_cache, out=None, lse=None, k_scale: float =
                        ctypes.byref(do), ctypes.byref(dl) if dl is not None else None,
                        _stream_ptr(stream)))
     return out, lse
+
+
+def ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None):
+    """Combine two attention states over disjoint key sets of the same rows;
+    returns (out, lse_out).  out / lse_out are allocated if None (out may be o_a
+    or o_b for an in-place merge)."""
+    import torch
+
+    if out is None:
+        out = torch.empty_like(o_a)
+    if lse_out is None:
+        lse_out = torch.empty_like(lse_a)
+    da, dla, db, dlb, do, dlo = (tensor_desc(o_a), tensor_desc(lse_a), tensor_desc(o_b),
+                                 tensor_desc(lse_b), tensor_desc(out), tensor_desc(lse_out))
+    _check(_lib.ak_merge_states(ctypes.byref(da), ctypes.byref(dla), ctypes.byref(db),
+                                ctypes.byref(dlb), ctypes.byref(do), ctypes.byref(dlo),
+                                _stream_ptr(stream)))
+    return out, lse_out
 
 
 def ak_plan_info(plan: Plan) -> dict:

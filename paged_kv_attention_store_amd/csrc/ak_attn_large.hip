@@ -203,15 +203,18 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
   };
 
   // ---- prologue: offsets of blocks 0 and 1, block 0 staged, page ids of block 2 in flight
+  // (an empty KV range -- a non-causal request without pages -- has no blocks)
   int64_t page_next = 0;
-  if (wave == 0) {
+  if (nb > 0 && wave == 0) {
     put_offsets(0, page_of(0), 0);
     if (nb > 1) put_offsets(1, page_of(1), 1);
     if (nb > 2) page_next = page_of(2);
   }
   __syncthreads();
-  load_block(0);
-  store_block(0);
+  if (nb > 0) {
+    load_block(0);
+    store_block(0);
+  }
   __syncthreads();
 
   for (int b = 0; b < nb; ++b) {
@@ -618,9 +621,12 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  // ---- prologue: block 0 copied, page ids of block 1 loaded
-  load_pages(0, raw);
-  issue_copy(k0s, v0s, 0, raw);
+  // ---- prologue: block 0 copied, page ids of block 1 loaded (an empty KV range
+  // -- a non-causal request without pages -- has no blocks)
+  if (nb > 0) {
+    load_pages(0, raw);
+    issue_copy(k0s, v0s, 0, raw);
+  }
   if (nb > 1) load_pages(1, raw);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();

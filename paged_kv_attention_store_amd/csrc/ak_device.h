@@ -132,6 +132,18 @@ struct AttnArgs {
   float v_scale;
 };
 
+struct Merge2Args {          // two (out, lse) states of the same rows
+  const void* oa;
+  const void* ob;
+  const float* la;
+  const float* lb;
+  void* out;
+  float* lse;                // may be null
+  int64_t a_st, a_sh, b_st, b_sh, o_st, o_sh;   // o_a, o_b, out strides (elements)
+  int64_t la_st, la_sh, lb_st, lb_sh, l_st, l_sh;
+  int32_t T, H;
+};
+
 struct MergeArgs {
   const MergeJob* jobs;
   const float* part_o;

@@ -34,6 +34,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, int n_items, int D, hipStream_t s)
 
 // out dtype: AK_F32 or AK_BF16.
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t s);
+hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s);
 
 // Physical page holding KV position t of a request whose pages start at
 // kv_indices[page_off]; the position's row inside the page is t & (B - 1).

@@ -8,6 +8,7 @@
 //
 // One wavefront per (query token, query head) job, each lane owning D/64
 // consecutive columns; bandwidth-bound (reads S * (D + 1) floats per job).
+// The same combination of two states given as tensors backs ak_merge_states.
 
 #include "ak_launch.h"
 
@@ -60,7 +61,67 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
         wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
+// Two states given as tensors (the public merge): one wavefront per (token,
+// head), lane owning D/64 consecutive columns; LSEs in base e.
+template <int D, int DT>
+__global__ __launch_bounds__(256) void merge2_kernel(Merge2Args a) {
+  constexpr int PER = D / 64;
+  const int64_t job = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (job >= (int64_t)a.T * a.H) return;
+  const int64_t t = job / a.H, h = job - t * a.H;
+  const float la = a.la[t * a.la_st + h * a.la_sh];
+  const float lb = a.lb[t * a.lb_st + h * a.lb_sh];
+  const float m = fmaxf(la, lb);
+  float wa = 0.f, wb = 0.f;
+  if (m != -INFINITY) {
+    wa = __expf(la - m);   // exactly 1 for the larger state; 0 for a -inf state
+    wb = __expf(lb - m);
+  }
+  const float wsum = wa + wb;
+  const float ia = wsum > 0.f ? wa / wsum : 0.f, ib = wsum > 0.f ? wb / wsum : 0.f;
+  float va[PER], vb[PER];
+  const int64_t ca = t * a.a_st + h * a.a_sh + lane * PER;
+  const int64_t cb = t * a.b_st + h * a.b_sh + lane * PER;
+  if (DT == AK_F32) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      va[i] = static_cast<const float*>(a.oa)[ca + i];
+      vb[i] = static_cast<const float*>(a.ob)[cb + i];
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      va[i] = bf16_bits_to_f32(static_cast<const uint16_t*>(a.oa)[ca + i]);
+      vb[i] = bf16_bits_to_f32(static_cast<const uint16_t*>(a.ob)[cb + i]);
+    }
+  }
+  const int64_t co = t * a.o_st + h * a.o_sh + lane * PER;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    // a weight of 0 drops its state even where that state holds no finite data
+    const float v = (ia > 0.f ? ia * va[i] : 0.f) + (ib > 0.f ? ib * vb[i] : 0.f);
+    if (DT == AK_F32)
+      static_cast<float*>(a.out)[co + i] = v;
+    else
+      static_cast<uint16_t*>(a.out)[co + i] = (uint16_t)f32_to_bf16_bits(v);
+  }
+  if (a.lse && lane == 0) a.lse[t * a.l_st + h * a.l_sh] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 }  // namespace
+
+hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s) {
+  const int64_t jobs = (int64_t)a.T * a.H;
+  if (jobs <= 0) return hipSuccess;
+  dim3 grid((unsigned)((jobs + 3) / 4));
+  if (D == 64 && dtype == AK_F32) hipLaunchKernelGGL((merge2_kernel<64, AK_F32>), grid, dim3(256), 0, s, a);
+  else if (D == 128 && dtype == AK_F32) hipLaunchKernelGGL((merge2_kernel<128, AK_F32>), grid, dim3(256), 0, s, a);
+  else if (D == 64 && dtype == AK_BF16) hipLaunchKernelGGL((merge2_kernel<64, AK_BF16>), grid, dim3(256), 0, s, a);
+  else if (D == 128 && dtype == AK_BF16) hipLaunchKernelGGL((merge2_kernel<128, AK_BF16>), grid, dim3(256), 0, s, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
 
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t s) {
   if (a.n_jobs <= 0) return hipSuccess;

@@ -95,7 +95,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       L = (pages - 1) * B + last_page_len[r];
     }
     if (L > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: KV length exceeds 2^30");
-    if (n > L) {
+    if (causal && n > L) {   // the causal diagonal is aligned to the sequence end
       std::ostringstream os;
       os << "ak_plan: request " << r << " has " << n << " queries but only " << L << " KV tokens";
       return fail(AK_ERR_BAD_LENGTHS, os.str());

@@ -590,6 +590,69 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   return AK_OK;
 }
 
+extern "C" ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a,
+                                     const ak_tensor* o_b, const ak_tensor* lse_b, ak_tensor* out,
+                                     ak_tensor* lse_out, void* stream) {
+  if (!o_a || !lse_a || !o_b || !lse_b || !out)
+    return fail(AK_ERR_INVALID_ARG, "ak_merge_states: null tensor descriptor");
+  for (const ak_tensor* t : {o_a, o_b, static_cast<const ak_tensor*>(out)})
+    if (t->ndim != 3) return fail(AK_ERR_INVALID_ARG, "ak_merge_states: states must be [T, H, D]");
+  for (const ak_tensor* t : {lse_a, lse_b})
+    if (t->ndim != 2) return fail(AK_ERR_INVALID_ARG, "ak_merge_states: lse must be [T, H]");
+  if (lse_out && lse_out->ndim != 2) return fail(AK_ERR_INVALID_ARG, "ak_merge_states: lse must be [T, H]");
+  const int64_t T = out->shape[0], H = out->shape[1], D = out->shape[2];
+  for (const ak_tensor* t : {o_a, o_b})
+    if (t->shape[0] != T || t->shape[1] != H || t->shape[2] != D)
+      return fail(AK_ERR_SHAPE_MISMATCH, "ak_merge_states: o_a, o_b and out shapes differ");
+  for (const ak_tensor* t : {lse_a, lse_b, static_cast<const ak_tensor*>(lse_out)})
+    if (t && (t->shape[0] != T || t->shape[1] != H))
+      return fail(AK_ERR_SHAPE_MISMATCH, "ak_merge_states: lse shape differs from [T, H]");
+  const int32_t dt = out->dtype;
+  if ((dt != AK_F32 && dt != AK_BF16) || o_a->dtype != dt || o_b->dtype != dt)
+    return fail(AK_ERR_UNSUPPORTED, "ak_merge_states: states must all be F32 or all BF16");
+  for (const ak_tensor* t : {lse_a, lse_b, static_cast<const ak_tensor*>(lse_out)})
+    if (t && t->dtype != AK_F32) return fail(AK_ERR_UNSUPPORTED, "ak_merge_states: lse must be F32");
+  if (D != 64 && D != 128) return fail(AK_ERR_UNSUPPORTED, "ak_merge_states: head_dim must be 64 or 128");
+  if (T == 0 || H == 0) return AK_OK;
+  if (T > INT32_MAX || H > INT32_MAX) return fail(AK_ERR_UNSUPPORTED, "ak_merge_states: too many rows");
+  for (const ak_tensor* t : {o_a, o_b, static_cast<const ak_tensor*>(out), lse_a, lse_b,
+                             static_cast<const ak_tensor*>(lse_out)})
+    if (t && !t->data) return fail(AK_ERR_INVALID_ARG, "ak_merge_states: null data pointer");
+  const int eb = dt == AK_F32 ? 4 : 2;
+  for (const ak_tensor* t : {o_a, o_b, static_cast<const ak_tensor*>(out)})
+    if (t->stride[2] != 1 || !aligned16(t->data) || (t->stride[0] * eb) % 16 || (t->stride[1] * eb) % 16)
+      return fail(AK_ERR_UNSUPPORTED, "ak_merge_states: rows must be contiguous and 16-byte aligned");
+  Merge2Args m{};
+  m.oa = o_a->data;
+  m.ob = o_b->data;
+  m.la = static_cast<const float*>(lse_a->data);
+  m.lb = static_cast<const float*>(lse_b->data);
+  m.out = out->data;
+  m.lse = lse_out ? static_cast<float*>(lse_out->data) : nullptr;
+  m.a_st = o_a->stride[0];
+  m.a_sh = o_a->stride[1];
+  m.b_st = o_b->stride[0];
+  m.b_sh = o_b->stride[1];
+  m.o_st = out->stride[0];
+  m.o_sh = out->stride[1];
+  m.la_st = lse_a->stride[0];
+  m.la_sh = lse_a->stride[1];
+  m.lb_st = lse_b->stride[0];
+  m.lb_sh = lse_b->stride[1];
+  m.l_st = lse_out ? lse_out->stride[0] : 0;
+  m.l_sh = lse_out ? lse_out->stride[1] : 0;
+  m.T = (int32_t)T;
+  m.H = (int32_t)H;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  {
+    ProfScope ps(3, s);
+    e = launch_merge2(m, (int)D, dt, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "ak_merge_states: launch");
+  return AK_OK;
+}
+
 // ------------------------------------------------------------- diagnostics
 
 extern "C" const char* ak_last_error(void) { return g_err.c_str(); }

@@ -106,8 +106,9 @@ def _new_token_slots(req_pages, kv_lens, q_lens, page_size):
         n, L = int(q_lens[r]), int(kv_lens[r])
         for j in range(n):
             p = L - n + j
-            slots.append(int(req_pages[r][p // page_size]) * page_size + p % page_size)
-            rows.append(row)
+            if p >= 0:   # a query before the cached positions (non-causal, n > L) stores nothing
+                slots.append(int(req_pages[r][p // page_size]) * page_size + p % page_size)
+                rows.append(row)
             row += 1
     return np.asarray(slots, dtype=np.int64), np.asarray(rows, dtype=np.int64)
 

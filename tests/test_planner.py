@@ -246,3 +246,17 @@ def test_large_split_of_few_long_jobs(seed):
         assert len(parts) >= 2
         n_merge += key[3]
     assert info["small_items"] == 0 and n_merge == info["merge_jobs"]
+
+
+# ------------------------------------------------------- non-causal segments
+
+def test_noncausal_allows_more_queries_than_keys():
+    # causal = 0: every key is visible, positions do not matter, so n_r > L_r is a
+    # valid request (the prefix segment of a two-segment extend); L_r = 0 is the
+    # empty state.  With causal = 1 the same batch is rejected.
+    qo, kv, last = [0, 5, 45, 48], [0, 1, 1, 5], [3, 0, 16]
+    assert _status(lambda: host_plan(qo, kv, last, causal=True)) == ak.AK_ERR_BAD_LENGTHS
+    p, items = check_coverage(np.array(qo), np.array(kv), np.array(last), 16, 8, 2, False, -1)
+    # the request without pages is still planned (its rows get the empty state)
+    assert set(items[:, 0].tolist()) == {0, 1, 2}
+    assert np.all(items[items[:, 0] == 1][:, 4:6] == 0)
