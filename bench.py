@@ -16,7 +16,8 @@ duration from HIP events recorded around every launch on the launch stream.
 Further workloads (--also) are reported under their names: the ragged extend
 batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
 the mixed chunked-prefill + decode step with full and sliding-window layers
-("mixed"), and the fp8 long-context decode ("longfp8").
+("mixed"), the fp8 long-context decode ("longfp8"), and decode requests sharing
+a 4096-token prefix run plainly and as a cascade ("cascade").
 
 The CPU baseline times the float64 oracle on a sample of the decode batch.
 """
@@ -304,11 +305,75 @@ def cpu_baseline(wl, budget_s=12.0, n_req=16):
 
 # -------------------------------------------------------------------- main
 
+def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
+    """Shared-prefix decode two ways on the same caches: plain (one plan over every
+    request's full page list) and cascade (the shared pages once for all queries
+    as one non-causal request, each request's own pages, then ak_merge_states).
+    Device time per layer from events on the stream, plans built beforehand."""
+    log(f"[bench] {wl.name}: R={wl.batch_size} KV tokens={int(wl.kv_lens.sum())} "
+        f"shared pages={wl.extra['shared_pages']} layers={n_layers}")
+    layers = make_layers(wl, n_layers, dev)
+    T, hq, hkv, D, B = wl.total_q, wl.num_qo_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
+    k = wl.extra["shared_pages"]
+    idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
+    plain = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B)
+    idx_s = torch.from_numpy(wl.kv_indices[:k].astype(np.int32)).to(dev)
+    shared = ak.ak_plan([0, T], [0, k], idx_s, [B], hq, hkv, D, B, causal=False)
+    sx = np.concatenate([wl.kv_indices[wl.kv_indptr[r] + k:wl.kv_indptr[r + 1]]
+                         for r in range(wl.batch_size)]).astype(np.int32)
+    si = np.concatenate([[0], np.cumsum(np.diff(wl.kv_indptr) - k)]).astype(np.int32)
+    idx_x = torch.from_numpy(sx).to(dev)
+    suffix = ak.ak_plan(wl.qo_indptr, si, idx_x, wl.last_page_len, hq, hkv, D, B)
+    o1, o2 = torch.empty_like(layers[0]["q"]), torch.empty_like(layers[0]["q"])
+    l1 = torch.empty(T, hq, dtype=torch.float32, device=dev)
+    l2 = torch.empty_like(l1)
+
+    def plain_pass():
+        for L in layers:
+            ak.ak_run(plain, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+
+    def cascade_pass():
+        for L in layers:
+            ak.ak_run(shared, L["q"], L["kc"], L["vc"], out=o1, lse=l1)
+            ak.ak_run(suffix, L["q"], L["kc"], L["vc"], out=o2, lse=l2)
+            ak.ak_merge_states(o1, l1, o2, l2, out=L["out"], lse_out=L["lse"])
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (steps * n_layers)
+
+    plain_us, cascade_us = timed(plain_pass), timed(cascade_pass)
+    per_tok = hkv * D * 2 * EB[wl.kv_dtype]
+    plain_bytes = decode_bytes(wl)
+    cascade_bytes = plain_bytes - (wl.batch_size - 1) * k * B * per_tok
+    res = {"workload": wl.name, "layers": n_layers, "shared_tokens": k * B,
+           "plain_us_per_layer": round(plain_us, 1), "cascade_us_per_layer": round(cascade_us, 1),
+           "speedup": round(plain_us / cascade_us, 2),
+           "plain_GBs": round(plain_bytes / (plain_us * 1e-6) / 1e9, 1),
+           "cascade_GBs": round(cascade_bytes / (cascade_us * 1e-6) / 1e9, 1),
+           "plain_bytes": plain_bytes, "cascade_bytes": cascade_bytes}
+    log(f"[bench] {wl.name}: plain {plain_us:.1f} us/layer ({res['plain_GBs']} GB/s), cascade "
+        f"{cascade_us:.1f} us/layer ({res['cascade_GBs']} GB/s of its own bytes), "
+        f"x{res['speedup']}")
+    del layers
+    torch.cuda.empty_cache()
+    return res
+
+
 WORKLOADS = {
     # name: (factory, layers with distinct caches)
     "prefill": (lambda W: W.config(3), 2),
     "mixed": (lambda W: W.config(4), 4),
     "longfp8": (lambda W: W.config(5), 4),
+    "cascade": (lambda W: W.shared_prefix_decode(), 8),
 }
 
 
@@ -340,6 +405,9 @@ def main():
     extra = {}
     for name in [x for x in args.also.split(",") if x]:
         fac, nl = WORKLOADS[name]
+        if name == "cascade":
+            extra[name] = measure_cascade(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
+            continue
         extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
     traffic = measured_traffic()
@@ -383,6 +451,9 @@ def main():
         "copy_GBs": copy,
     }
     for name, r in extra.items():
+        if name == "cascade":
+            line[name] = r
+            continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
              "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1),
              "plan_host_us": round(r["plan_host_us"], 1)}

@@ -207,6 +207,27 @@ def llama70b_long_decode(seed: int = 5, R: int = 8, L: int = 131072) -> Workload
                      True, (-1,))
 
 
+def shared_prefix_decode(seed: int = 6, R: int = 64, prefix_pages: int = 256,
+                         suffix=(256, 2048)) -> Workload:
+    """64 decode requests sharing their first 4096 tokens (256 pages of 16: one
+    system prompt) followed by unique suffixes of U{256..2048} tokens; 32/8 heads,
+    D = 128, bf16.  Every request's page list starts with the same pages;
+    `extra['shared_pages']` is their count (the cascade's shared segment)."""
+    g_len, g_perm, _, _ = _streams(seed)
+    B = 16
+    kv_lens = prefix_pages * B + g_len.integers(suffix[0], suffix[1], size=R, endpoint=True)
+    wl = _assemble("shared_prefix_decode_bf16", seed, np.ones(R, dtype=np.int64), kv_lens, B,
+                   g_perm, 32, 8, 128, "bf16", "bf16", True, (-1,))
+    # request r's first prefix_pages pages become request 0's (its own first pages
+    # stay allocated in the pool, unused); the new token sits in an unshared page
+    for r in range(1, R):
+        wl.req_pages[r][:prefix_pages] = wl.req_pages[0][:prefix_pages]
+        a = int(wl.kv_indptr[r])
+        wl.kv_indices[a:a + prefix_pages] = wl.kv_indices[:prefix_pages]
+    wl.extra["shared_pages"] = prefix_pages
+    return wl
+
+
 CONFIGS = {
     1: tiny_decode,
     2: llama8b_decode,
