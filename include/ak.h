@@ -101,6 +101,62 @@ typedef struct {
 ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v, const ak_tensor* slot_mapping,
                       ak_tensor* k_cache, ak_tensor* v_cache, void* stream);
 
+/* --------------------------------------------------------------- metadata */
+
+/* ak_csr_from_block_table -- the CSR page table of a batch from its 2-D block
+ * table, on the device.
+ *
+ * Defines ("vLLM attention backend", "From a 2-D block table to a CSR page
+ * table"; checked against the page's worked example): request r owns the first
+ * pages_r = ceil(L_r / B) entries of its block-table row, and
+ *   kv_indptr[0] = 0,  kv_indptr[r + 1] = kv_indptr[r] + pages_r,
+ *   kv_indices[kv_indptr[r] + k] = block_table[r][k]   for k < pages_r,
+ *   last_page_len[r] = L_r - (pages_r - 1) * B  (in [1, B]; 0 when L_r = 0).
+ *
+ *   block_table    device int32 [batch_size, max_pages], row-major, rows
+ *                  contiguous; entries past pages_r are never read.
+ *   seq_lens       device int32 [batch_size], the KV length L_r of each request
+ *                  (this step's tokens included).  A length outside
+ *                  [0, max_pages * B] is clamped into it (the row holds no more).
+ *   kv_indptr      device int32 [batch_size + 1], written.
+ *   kv_indices     device int32 [capacity], written in [0, kv_indptr[batch_size]);
+ *                  entries at or past `capacity` are dropped, so a caller that
+ *                  cannot bound the total reads kv_indptr[batch_size] back.
+ *   last_page_len  device int32 [batch_size], written.
+ *
+ * Outputs are caller-owned; the result is the plain definition above, bit for
+ * bit (integer work).  Page ids are copied unchecked.  Enqueued on `stream`,
+ * no host synchronisation, no allocation.  Errors: AK_ERR_INVALID_ARG (null
+ * pointer, batch_size < 0, page_size < 1, max_pages < 0, capacity < 0), AK_ERR_HIP.
+ * batch_size = 0 writes kv_indptr[0] = 0 only. */
+ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_pages,
+                                  const int32_t* seq_lens, int32_t batch_size, int32_t page_size,
+                                  int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
+                                  int32_t* last_page_len, void* stream);
+
+/* ak_slot_mapping -- the cache slot of every new token of a step, on the device.
+ *
+ * Defines ("vLLM attention backend", "Write the KV first" and the worked
+ * example: position 127 of a request whose eighth page is 10 lands in slot 175
+ * for B = 16): the n_r = qo_indptr[r + 1] - qo_indptr[r] new tokens of request
+ * r are its last n_r positions, so token qo_indptr[r] + j has position
+ * p = L_r - n_r + j and slot block_table[r][p / B] * B + p % B.
+ *
+ *   block_table   device int32 [batch_size, max_pages], as above.
+ *   qo_indptr     device int32 [batch_size + 1], starting at 0, non-decreasing.
+ *   seq_lens      device int32 [batch_size], L_r with this step's tokens.
+ *   slot_mapping  device int64 [num_tokens], written: the slot, or -1 for a
+ *                 token past qo_indptr[batch_size] (padding of a fixed-size
+ *                 batch) and for a position outside [0, max_pages * B).  The
+ *                 result feeds ak_store_kv, which skips negative slots.
+ *
+ * Enqueued on `stream`; no synchronisation, no allocation.  Errors:
+ * AK_ERR_INVALID_ARG (null pointer, negative size, page_size < 1), AK_ERR_HIP.
+ * num_tokens = 0 launches nothing. */
+ak_status ak_slot_mapping(const int32_t* block_table, int64_t max_pages, const int32_t* qo_indptr,
+                          const int32_t* seq_lens, int32_t batch_size, int32_t page_size,
+                          int64_t* slot_mapping, int64_t num_tokens, void* stream);
+
 /* ------------------------------------------------------------------- plan */
 
 typedef struct ak_plan_t ak_plan_t;    /* opaque; owned by the library */

@@ -44,7 +44,7 @@ AK_PLAN_HOST_ONLY = 1
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
-            "ak_merge_states",
+            "ak_merge_states", "ak_csr_from_block_table", "ak_slot_mapping",
             "ak_profile_read", "ak_version", "ak_fp8_to_bf16"]
 
 
@@ -90,6 +90,12 @@ def _load():
     lib.ak_plan_export.restype = ctypes.c_int
     lib.ak_merge_states.argtypes = [P(AkTensor)] * 6 + [ctypes.c_void_p]
     lib.ak_merge_states.restype = ctypes.c_int
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.ak_csr_from_block_table.argtypes = [vp, i64, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
+                                            i64, vp, vp]
+    lib.ak_csr_from_block_table.restype = ctypes.c_int
+    lib.ak_slot_mapping.argtypes = [vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
+    lib.ak_slot_mapping.restype = ctypes.c_int
     lib.ak_gather_slots.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.ak_gather_slots.restype = ctypes.c_int
     lib.ak_profile_enable.argtypes = [ctypes.c_int32]
@@ -295,6 +301,75 @@ def ak_plan_export(plan: Plan):
 def ak_gather_slots(plan: Plan, slots, stream=None) -> None:
     """Write every request's KV slots (device int64 tensor of sum L entries)."""
     _check(_lib.ak_gather_slots(plan.handle, ctypes.c_void_p(slots.data_ptr()), _stream_ptr(stream)))
+
+
+def _dev_i32_matrix(t, name):
+    if t.dtype != _torch().int32 or t.dim() != 2 or not t.is_contiguous() or not t.is_cuda:
+        raise AkError(-1, f"{name}: expected a contiguous device int32 [rows, cols] tensor")
+    return t
+
+
+def _dev_i32_vector(t, n, name):
+    if t.dtype != _torch().int32 or t.dim() != 1 or t.numel() < n or not t.is_cuda:
+        raise AkError(-1, f"{name}: expected a device int32 vector of at least {n} entries")
+    return t
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def ak_csr_from_block_table(block_table, seq_lens, page_size: int, kv_indices=None,
+                            kv_indptr=None, last_page_len=None, stream=None):
+    """Build (kv_indptr, kv_indices, last_page_len) from a device block table
+    [R, max_pages] and device seq_lens [R] (all int32).  kv_indices defaults to
+    R * max_pages entries, enough for any lengths; the valid prefix is
+    kv_indices[:kv_indptr[R]]."""
+    torch = _torch()
+    _dev_i32_matrix(block_table, "block_table")
+    R, max_pages = block_table.shape
+    _dev_i32_vector(seq_lens, R, "seq_lens")
+    dev = block_table.device
+    if kv_indptr is None:
+        kv_indptr = torch.empty(R + 1, dtype=torch.int32, device=dev)
+    if last_page_len is None:
+        last_page_len = torch.empty(R, dtype=torch.int32, device=dev)
+    if kv_indices is None:
+        kv_indices = torch.empty(max(R * max_pages, 1), dtype=torch.int32, device=dev)
+    _dev_i32_vector(kv_indptr, R + 1, "kv_indptr")
+    _dev_i32_vector(last_page_len, R, "last_page_len")
+    _dev_i32_vector(kv_indices, 0, "kv_indices")
+    _check(_lib.ak_csr_from_block_table(
+        ctypes.c_void_p(block_table.data_ptr()), max_pages, ctypes.c_void_p(seq_lens.data_ptr()),
+        R, int(page_size), ctypes.c_void_p(kv_indptr.data_ptr()),
+        ctypes.c_void_p(kv_indices.data_ptr()), kv_indices.numel(),
+        ctypes.c_void_p(last_page_len.data_ptr()), _stream_ptr(stream)))
+    return kv_indptr, kv_indices, last_page_len
+
+
+def ak_slot_mapping(block_table, qo_indptr, seq_lens, page_size: int, num_tokens=None, out=None,
+                    stream=None):
+    """Slots of every new token (device int64 [num_tokens]; -1 for padding) from a
+    device block table [R, max_pages], qo_indptr [R + 1] and seq_lens [R] (int32).
+    num_tokens defaults to the batch's token count, which costs a device read."""
+    torch = _torch()
+    _dev_i32_matrix(block_table, "block_table")
+    R, max_pages = block_table.shape
+    _dev_i32_vector(qo_indptr, R + 1, "qo_indptr")
+    _dev_i32_vector(seq_lens, R, "seq_lens")
+    if out is None:
+        if num_tokens is None:
+            num_tokens = int(qo_indptr[R].item())
+        out = torch.empty(num_tokens, dtype=torch.int64, device=block_table.device)
+    if out.dtype != torch.int64 or not out.is_contiguous() or not out.is_cuda:
+        raise AkError(-1, "slot_mapping: expected a contiguous device int64 tensor")
+    _check(_lib.ak_slot_mapping(
+        ctypes.c_void_p(block_table.data_ptr()), max_pages, ctypes.c_void_p(qo_indptr.data_ptr()),
+        ctypes.c_void_p(seq_lens.data_ptr()), R, int(page_size), ctypes.c_void_p(out.data_ptr()),
+        out.numel(), _stream_ptr(stream)))
+    return out
 
 
 KERNEL_KINDS = ["store_kv", "attn_small", "attn_large", "merge", "attn_f32"]

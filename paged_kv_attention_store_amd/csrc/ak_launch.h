@@ -35,6 +35,13 @@ hipError_t launch_attn_f32(const AttnArgs& a, int n_items, int D, hipStream_t s)
 // out dtype: AK_F32 or AK_BF16.
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t s);
 hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s);
+hipError_t launch_csr_from_block_table(const int32_t* block_table, int64_t row_stride,
+                                       const int32_t* seq_lens, int32_t R, int32_t B,
+                                       int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
+                                       int32_t* last_page_len, hipStream_t s);
+hipError_t launch_slot_mapping(const int32_t* block_table, int64_t row_stride, const int32_t* qo_indptr,
+                               const int32_t* seq_lens, int32_t R, int32_t B, int64_t* slot_mapping,
+                               int64_t N, hipStream_t s);
 
 // Physical page holding KV position t of a request whose pages start at
 // kv_indices[page_off]; the position's row inside the page is t & (B - 1).

@@ -713,6 +713,39 @@ extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* s
   return AK_OK;
 }
 
+extern "C" ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_pages,
+                                             const int32_t* seq_lens, int32_t batch_size,
+                                             int32_t page_size, int32_t* kv_indptr,
+                                             int32_t* kv_indices, int64_t capacity,
+                                             int32_t* last_page_len, void* stream) {
+  if (batch_size < 0 || page_size < 1 || max_pages < 0 || capacity < 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_csr_from_block_table: negative size or page_size < 1");
+  if (!kv_indptr || (batch_size > 0 && (!block_table || !seq_lens || !last_page_len)) ||
+      (capacity > 0 && !kv_indices))
+    return fail(AK_ERR_INVALID_ARG, "ak_csr_from_block_table: null pointer");
+  hipError_t e = launch_csr_from_block_table(block_table, max_pages, seq_lens, batch_size, page_size,
+                                             kv_indptr, kv_indices, capacity, last_page_len,
+                                             static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ak_csr_from_block_table");
+  return AK_OK;
+}
+
+extern "C" ak_status ak_slot_mapping(const int32_t* block_table, int64_t max_pages,
+                                     const int32_t* qo_indptr, const int32_t* seq_lens,
+                                     int32_t batch_size, int32_t page_size, int64_t* slot_mapping,
+                                     int64_t num_tokens, void* stream) {
+  if (batch_size < 0 || page_size < 1 || max_pages < 0 || num_tokens < 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_slot_mapping: negative size or page_size < 1");
+  if (num_tokens == 0) return AK_OK;
+  if (!qo_indptr || !slot_mapping || (batch_size > 0 && (!block_table || !seq_lens)))
+    return fail(AK_ERR_INVALID_ARG, "ak_slot_mapping: null pointer");
+  hipError_t e = launch_slot_mapping(block_table, max_pages, qo_indptr, seq_lens, batch_size,
+                                     page_size, slot_mapping, num_tokens,
+                                     static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "ak_slot_mapping");
+  return AK_OK;
+}
+
 extern "C" ak_status ak_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream) {
   if (n < 0 || (n % 8) != 0) return fail(AK_ERR_INVALID_ARG, "ak_fp8_to_bf16: n must be a multiple of 8");
   if (n == 0) return AK_OK;
