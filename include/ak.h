@@ -252,7 +252,9 @@ void ak_plan_destroy(ak_plan_t* plan);
  * AK_ERR_SHAPE_MISMATCH (T, Hq, Hkv, D or B disagree with the plan -- a plan
  * built for fewer heads is rejected, never run), AK_ERR_UNSUPPORTED (dtype
  * combination, misaligned rows), AK_ERR_HIP.  An empty plan returns AK_OK and
- * launches nothing. */
+ * launches nothing.  With a fixed plan (ak_plan_fixed) T is the plan's
+ * max_tokens, the launches cover its whole capacity whatever the live batch,
+ * and rows past qo_indptr[batch_size] of the last update are left untouched. */
 ak_status ak_run(const ak_plan_t* plan, const ak_tensor* q, const ak_tensor* k_cache,
                  const ak_tensor* v_cache, ak_tensor* out, ak_tensor* lse, void* stream);
 
@@ -286,11 +288,62 @@ ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak
                           const ak_tensor* lse_b, ak_tensor* out, ak_tensor* lse_out,
                           void* stream);
 
+/* ----------------------------------------------------------- fixed plans */
+
+/* ak_plan_fixed / ak_plan_update -- a plan whose device workspace never moves,
+ * for runs captured into a HIP graph.
+ *
+ * Follows "vLLM attention backend", the graph-capture section (stable device
+ * addresses; dynamic content written into stable buffers), "SGLang attention
+ * backend", the backend's graph duties (buffers sized by the largest batch,
+ * refreshed before each replay; host work kept out of the graph), and the
+ * graph section of "FlashInfer and the backend abstraction" (the tail of
+ * persistent scheduling metadata cleared so that stale entries write nothing).
+ *
+ * ak_plan_fixed allocates, once, a workspace sized for any batch of at most
+ * max_batch requests, max_tokens query tokens and max_pages pages: the work list
+ * with room for every split the planner may choose, the split partials and the
+ * merge list, all zeroed (a zero entry is padding: its workgroup exits at once).
+ * Geometry (heads, head_dim, page_size, causal, window) and opts are fixed with
+ * it and follow ak_plan.  `kv_indices` is the DEVICE int32 buffer of max_pages
+ * entries that every later batch's page ids are written into (borrowed; stable
+ * for the plan's lifetime).  The call synchronises opts->stream; it is never
+ * captured.
+ *
+ * ak_plan_update plans one batch (host arrays as in ak_plan, validated the same
+ * way) and writes its work list over the previous one with asynchronous copies
+ * on `stream`, padding out entries the previous batch used past the new one's
+ * end.  It must be issued on the stream that replays the runs, between replays,
+ * and outside capture.  The plan's workspace holds one batch: an update takes
+ * effect for every later replay.
+ *
+ * ak_run with a fixed plan launches every kernel over the capacity (fixed
+ * grids), so a run captured once replays correctly after any update.  Padding
+ * workgroups cost a few microseconds per run.
+ *
+ * The capacity always suffices for page_size >= 8, KV lengths up to
+ * max_splits * (1022 * page_size - 128) and num_kv_heads * sum L_r up to
+ * 8 * num_cus * 4096; beyond that ak_plan_update may return AK_ERR_UNSUPPORTED
+ * and leaves the plan as it was.
+ * Errors: AK_ERR_INVALID_ARG (null pointer, negative capacity, update of a
+ * non-fixed plan), AK_ERR_UNSUPPORTED, AK_ERR_SHAPE_MISMATCH (batch larger than
+ * the capacities), AK_ERR_BAD_INDPTR / AK_ERR_BAD_LENGTHS (as ak_plan),
+ * AK_ERR_OOM, AK_ERR_HIP.  With AK_PLAN_HOST_ONLY in opts->flags nothing is
+ * allocated or uploaded (for checking the work list and capacities). */
+ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_pages,
+                        const int32_t* kv_indices, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, int32_t causal, int32_t window,
+                        const ak_plan_opts* opts, ak_plan_t** plan);
+ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* last_page_len, int32_t batch_size, void* stream);
+
 /* ak_plan_info -- host-side summary of a plan (any plan, host-only included).
- * Writes up to 8 int64 values into `info` (caller-owned host array):
+ * Writes up to 12 int64 values into `info` (caller-owned host array):
  *   [0] batch_size  [1] total query rows T  [2] work items  [3] small-tile items
  *   [4] large-tile items  [5] split (request, KV head) units  [6] merge jobs
- *   [7] partial rows in the split workspace.
+ *   [7] partial rows in the split workspace; for a fixed plan the capacities
+ *   [8] small-tile items [9] large-tile items [10] merge jobs [11] partial rows
+ *   (0 for other plans).
  * Errors: AK_ERR_INVALID_ARG. */
 ak_status ak_plan_info(const ak_plan_t* plan, int64_t* info, int32_t n);
 

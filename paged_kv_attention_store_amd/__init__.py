@@ -44,7 +44,8 @@ AK_PLAN_HOST_ONLY = 1
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
-            "ak_merge_states", "ak_csr_from_block_table", "ak_slot_mapping",
+            "ak_merge_states", "ak_csr_from_block_table", "ak_slot_mapping", "ak_plan_fixed",
+            "ak_plan_update",
             "ak_profile_read", "ak_version", "ak_fp8_to_bf16"]
 
 
@@ -70,6 +71,12 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"libak.so not found at {LIB_PATH}; build it with "
                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    # torch ships its own HIP runtime and loads it by path; libak must bind to
+    # that same runtime (one runtime per process), so torch is loaded first
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # pragma: no cover - the host-only planner still works
+        pass
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     i32p = P(ctypes.c_int32)
@@ -78,6 +85,11 @@ def _load():
     lib.ak_plan.argtypes = [i32p, i32p, ctypes.c_void_p, i32p] + [ctypes.c_int32] * 7 + [
         P(AkPlanOpts), P(ctypes.c_void_p)]
     lib.ak_plan.restype = ctypes.c_int
+    lib.ak_plan_fixed.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p] + [
+        ctypes.c_int32] * 6 + [P(AkPlanOpts), P(ctypes.c_void_p)]
+    lib.ak_plan_fixed.restype = ctypes.c_int
+    lib.ak_plan_update.argtypes = [ctypes.c_void_p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_void_p]
+    lib.ak_plan_update.restype = ctypes.c_int
     lib.ak_plan_destroy.argtypes = [ctypes.c_void_p]
     lib.ak_plan_destroy.restype = None
     lib.ak_run.argtypes = [ctypes.c_void_p] + [P(AkTensor)] * 5 + [ctypes.c_void_p]
@@ -236,6 +248,51 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
     return Plan(h, num_qo_heads, num_kv_heads, head_dim, page_size, host_only, kv_indices)
 
 
+def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int,
+                  num_kv_heads: int, head_dim: int, page_size: int, causal: bool = True,
+                  window: int = -1, sm_scale: float | None = None, num_cus: int = 0,
+                  max_splits: int = 0, min_chunk: int = 0, host_only: bool = False,
+                  max_pages: int | None = None, stream=None) -> Plan:
+    """A plan with a fixed device workspace for graph capture.  kv_indices is the
+    stable device int32 buffer later batches write their page ids into (its size
+    is the page capacity); host-only plans take None and max_pages."""
+    opts = AkPlanOpts()
+    opts.sm_scale = float(sm_scale) if sm_scale else 0.0
+    opts.num_cus = int(num_cus)
+    opts.max_splits = int(max_splits)
+    opts.min_chunk = int(min_chunk)
+    opts.flags = AK_PLAN_HOST_ONLY if host_only else 0
+    opts.stream = None if host_only else _stream_ptr(stream)
+    idx_ptr = None
+    if kv_indices is not None and not host_only:
+        import torch
+
+        if kv_indices.dtype != torch.int32 or not kv_indices.is_contiguous():
+            raise TypeError("kv_indices must be a contiguous int32 device tensor")
+        idx_ptr = ctypes.c_void_p(kv_indices.data_ptr())
+        if max_pages is None:
+            max_pages = kv_indices.numel()
+    h = ctypes.c_void_p()
+    _check(_lib.ak_plan_fixed(int(max_batch), int(max_tokens), int(max_pages or 0), idx_ptr,
+                              num_qo_heads, num_kv_heads, head_dim, page_size, int(bool(causal)),
+                              int(window), ctypes.byref(opts), ctypes.byref(h)))
+    plan = Plan(h, num_qo_heads, num_kv_heads, head_dim, page_size, host_only, kv_indices)
+    plan.fixed = True
+    return plan
+
+
+def ak_plan_update(plan: Plan, qo_indptr, kv_indptr, last_page_len, stream=None) -> None:
+    """Plan a new batch into a fixed plan's workspace (host arrays as for ak_plan)."""
+    qo, qo_p = _host_i32(qo_indptr)
+    kv, kv_p = _host_i32(kv_indptr)
+    last, last_p = _host_i32(last_page_len)
+    R = len(qo) - 1
+    if len(kv) != R + 1 or len(last) != R:
+        raise ValueError("qo_indptr/kv_indptr need batch_size+1 entries, last_page_len batch_size")
+    _check(_lib.ak_plan_update(plan.handle, qo_p, kv_p, last_p, R,
+                               None if plan.host_only else _stream_ptr(stream)))
+
+
 def ak_plan_destroy(plan: Plan) -> None:
     if plan is not None and plan.handle is not None and plan.handle.value:
         _lib.ak_plan_destroy(plan.handle)
@@ -278,10 +335,11 @@ def ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None)
 
 
 def ak_plan_info(plan: Plan) -> dict:
-    buf = (ctypes.c_int64 * 8)()
-    _check(_lib.ak_plan_info(plan.handle, buf, 8))
+    buf = (ctypes.c_int64 * 12)()
+    _check(_lib.ak_plan_info(plan.handle, buf, 12))
     keys = ["batch_size", "total_q", "items", "small_items", "large_items", "split_units",
-            "merge_jobs", "partial_rows"]
+            "merge_jobs", "partial_rows", "cap_small_items", "cap_large_items", "cap_merge_jobs",
+            "cap_partial_rows"]
     return dict(zip(keys, [int(x) for x in buf]))
 
 

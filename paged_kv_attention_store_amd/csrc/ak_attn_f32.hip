@@ -22,6 +22,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   constexpr int PER = D / 64;
   __shared__ __align__(16) float qs[4][D];
   const Item it = a.items[blockIdx.x];
+  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
   const Req rq = a.reqs[it.r];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_f32(const AttnArgs& a, int n_items, int D, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128) {

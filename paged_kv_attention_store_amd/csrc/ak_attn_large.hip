@@ -674,6 +674,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128 && kv_dtype == AK_BF16) {

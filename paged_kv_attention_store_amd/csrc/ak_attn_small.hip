@@ -87,6 +87,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   __shared__ int32_t s_pages[kSmallMaxPages];
 
   const Item it = a.items[blockIdx.x];
+  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
   const Req rq = a.reqs[it.r];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -412,6 +413,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
   if (D == 128 && kv_dtype == AK_BF16) {

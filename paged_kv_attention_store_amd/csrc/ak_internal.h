@@ -49,6 +49,13 @@ struct MergeJob {      // one (query token, query head) finished from split part
   int32_t pad[3];
 };
 
+struct FixedCaps {     // capacities of a fixed plan
+  int32_t batch = 0;   // requests
+  int64_t tokens = 0;  // query tokens (the row count of q and out)
+  int64_t pages = 0;   // entries of the kv_indices buffer
+  int64_t small = 0, large = 0, merges = 0, partial_rows = 0;
+};
+
 }  // namespace ak
 
 struct ak_plan_t {
@@ -64,6 +71,11 @@ struct ak_plan_t {
   std::vector<ak::MergeJob> merges;
   int64_t partial_rows = 0;
   int64_t split_units = 0;
+  // fixed plan: capacities the workspace is sized for (kernels are launched over
+  // the whole capacity; entries past the live ones are padding with zero rows)
+  bool fixed = false;
+  ak::FixedCaps caps;
+  int64_t hw_small = 0, hw_large = 0, hw_merges = 0;   // entries uploaded so far
   const int32_t* kv_indices = nullptr;   // device, borrowed
   int64_t num_kv_pages = 0;
   // device workspace (one allocation)
@@ -88,5 +100,12 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           const int32_t* last_page_len, int32_t batch_size, int32_t num_qo_heads,
                           int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
                           int32_t window, const ak_plan_opts* opts, int32_t num_cus, ak_plan_t* p);
+
+// Upper bounds on what build_plan_host emits for any batch of at most
+// caps->batch requests and caps->tokens query tokens (fills small, large,
+// merges, partial_rows).  Guaranteed for page sizes >= 8 and KV lengths up to
+// max_splits * (1022 * page_size - 128) with Hkv * sum(L) <= 8 * num_cus * 4096.
+void fixed_capacities(int32_t Hkv, int32_t G, int32_t num_cus, const ak_plan_opts* opts,
+                      FixedCaps* caps);
 
 }  // namespace ak

@@ -23,6 +23,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   const int lane = threadIdx.x & 63;
   if (job >= a.n_jobs) return;
   const MergeJob jb = a.jobs[job];
+  if (jb.count == 0) return;   // padding job
   float m = -INFINITY;
   for (int s = 0; s < jb.count; ++s) m = fmaxf(m, a.part_lse[jb.pfirst + (int64_t)s * jb.pstride]);
   float acc[PER];
@@ -112,6 +113,7 @@ __global__ __launch_bounds__(256) void merge2_kernel(Merge2Args a) {
 }  // namespace
 
 hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   const int64_t jobs = (int64_t)a.T * a.H;
   if (jobs <= 0) return hipSuccess;
   dim3 grid((unsigned)((jobs + 3) / 4));
@@ -124,6 +126,7 @@ hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (a.n_jobs <= 0) return hipSuccess;
   dim3 grid((unsigned)((a.n_jobs + 3) / 4));
 #define AK_MERGE_CASE(DD, O)                                                \

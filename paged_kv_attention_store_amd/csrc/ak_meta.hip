@@ -109,6 +109,7 @@ hipError_t launch_csr_from_block_table(const int32_t* block_table, int64_t row_s
                                        const int32_t* seq_lens, int32_t R, int32_t B,
                                        int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
                                        int32_t* last_page_len, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, seq_lens, R, B, row_stride,
                      kv_indptr, last_page_len);
   hipError_t e = hipGetLastError();
@@ -121,6 +122,7 @@ hipError_t launch_csr_from_block_table(const int32_t* block_table, int64_t row_s
 hipError_t launch_slot_mapping(const int32_t* block_table, int64_t row_stride, const int32_t* qo_indptr,
                                const int32_t* seq_lens, int32_t R, int32_t B, int64_t* slot_mapping,
                                int64_t N, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (N <= 0) return hipSuccess;
   hipLaunchKernelGGL(slots_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, block_table,
                      row_stride, qo_indptr, seq_lens, R, B, slot_mapping, N);

@@ -309,4 +309,37 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   return AK_OK;
 }
 
+// Bounds behind a fixed plan's workspace, following the planner above:
+//  * small units (<= kSmallRows rows) number at most Hkv * min(batch, tokens); a
+//    unit of len KV tokens gets at most ceil(len / chunk) parts and the chunk is
+//    at least 1/(8 num_cus) of all small-unit KV, so all parts together number at
+//    most units + 8 num_cus (inside the guaranteed range the 4096-token chunk cap
+//    and the page-table span never bind);
+//  * large jobs number at most Hkv * (ceil(tokens G / kLargeRows) + requests with
+//    more than kSmallRows rows); splitting adds at most sum(t) / (share - kSegCost)
+//    segments, and share >= max(sum cost / num_cus, 2 kMinPartTiles + kSegCost)
+//    bounds that by 19/16 num_cus, which also bounds the split jobs;
+//  * partial rows and merge jobs follow from the rows of split units and jobs.
+void fixed_capacities(int32_t Hkv, int32_t G, int32_t num_cus, const ak_plan_opts* opts,
+                      FixedCaps* c) {
+  const int64_t S = (opts && opts->max_splits > 0) ? opts->max_splits : 64;
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t R = c->batch, T = c->tokens;
+  const int64_t rows_all = T * G * Hkv;               // unit rows over every KV head
+  const int64_t units = (int64_t)Hkv * std::min<int64_t>(R, T);
+  c->small = std::min<int64_t>(units * S, units + 8 * cus);
+  int64_t part_small = std::min<int64_t>((int64_t)kSmallRows * c->small, S * rows_all);
+  int64_t merge_small = std::min<int64_t>((int64_t)kSmallRows * units, rows_all);
+  if (c->small == 0) part_small = merge_small = 0;
+  // requests with more than kSmallRows rows have at least kSmallRows / G + 1 tokens
+  const int64_t r_large = std::min<int64_t>(R, T / (kSmallRows / G + 1));
+  const int64_t jobs = r_large == 0 ? 0 : Hkv * (ceil_div(T * G, kLargeRows) + r_large);
+  const int64_t extra = ceil_div(19 * cus, 16);
+  c->large = jobs == 0 ? 0 : jobs + extra;
+  const int64_t part_large = jobs == 0 ? 0 : std::min<int64_t>(2 * (int64_t)kLargeRows * extra, S * rows_all);
+  const int64_t merge_large = jobs == 0 ? 0 : std::min<int64_t>((int64_t)kLargeRows * extra, rows_all);
+  c->partial_rows = part_small + part_large;
+  c->merges = merge_small + merge_large;
+}
+
 }  // namespace ak

@@ -78,6 +78,8 @@ struct ProfScope {
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(int k, hipStream_t st) : kind(k), s(st) {
     if (!g_prof.on) return;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     std::lock_guard<std::mutex> lk(g_prof.mu);
     a = g_prof.get();
     b = g_prof.get();
@@ -305,6 +307,7 @@ void return_ws(Workspace& w) {
 
 struct ak_plan_private : ak_plan_t {
   ak::Workspace ws;
+  ak_plan_opts fixed_opts{};   // planner options of a fixed plan, reused by every update
 };
 
 namespace ak {
@@ -446,8 +449,201 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
 extern "C" void ak_plan_destroy(ak_plan_t* plan) {
   if (!plan) return;
   auto* pp = static_cast<ak_plan_private*>(plan);
-  return_ws(pp->ws);     // the workspace's event covers its last use
+  if (pp->fixed) {
+    // a fixed plan owns its workspace; hipFree waits for work still using it
+    if (pp->ws.done) (void)hipEventSynchronize(pp->ws.done);
+    release_ws(pp->ws);
+  } else {
+    return_ws(pp->ws);   // the workspace's event covers its last use
+  }
   recycle_plan(pp);
+}
+
+// ------------------------------------------------------------- fixed plans
+
+namespace ak {
+namespace {
+
+struct FixedLayout {
+  size_t req, small, large, merge, meta, po, pl, total;
+};
+
+FixedLayout fixed_layout(const FixedCaps& c, int D) {
+  FixedLayout l{};
+  l.req = 0;
+  l.small = l.req + align256((size_t)c.batch * sizeof(Req));
+  l.large = l.small + align256((size_t)c.small * sizeof(Item));
+  l.merge = l.large + align256((size_t)c.large * sizeof(Item));
+  l.meta = l.merge + align256((size_t)c.merges * sizeof(MergeJob));
+  l.po = l.meta;
+  l.pl = l.po + align256((size_t)c.partial_rows * D * sizeof(float));
+  l.total = l.pl + align256((size_t)c.partial_rows * sizeof(float));
+  return l;
+}
+
+}  // namespace
+}  // namespace ak
+
+extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_pages,
+                                   const int32_t* kv_indices, int32_t num_qo_heads,
+                                   int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                                   int32_t causal, int32_t window, const ak_plan_opts* opts,
+                                   ak_plan_t** plan) {
+  if (!plan) return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: null output pointer");
+  *plan = nullptr;
+  if (max_batch < 0 || max_tokens < 0 || max_pages < 0)
+    return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: negative capacity");
+  if (max_tokens > INT32_MAX / 64 || max_pages > INT32_MAX)
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: capacity too large");
+  const bool host_only = opts && (opts->flags & AK_PLAN_HOST_ONLY);
+  auto* p = new_plan();
+  if (!p) return fail(AK_ERR_OOM, "ak_plan_fixed: out of host memory");
+  int dev = 0;
+  int cus = opts && opts->num_cus > 0 ? opts->num_cus : 0;
+  if (!host_only) {
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+      recycle_plan(p);
+      return hip_fail(e, "ak_plan_fixed: hipGetDevice");
+    }
+    if (cus == 0) cus = device_cus(dev);
+  }
+  if (cus == 0) cus = 256;
+  // the geometry is validated by planning an empty batch
+  ak_status st = build_plan_host(nullptr, nullptr, nullptr, 0, num_qo_heads, num_kv_heads, head_dim,
+                                 page_size, causal, window, opts, cus, p);
+  if (st != AK_OK) {
+    recycle_plan(p);
+    return st;
+  }
+  if (!host_only && max_pages > 0 && !kv_indices) {
+    recycle_plan(p);
+    return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: null kv_indices buffer");
+  }
+  p->fixed = true;
+  p->host_only = host_only;
+  p->device = dev;
+  p->kv_indices = kv_indices;
+  if (opts) p->fixed_opts = *opts;
+  p->fixed_opts.stream = nullptr;
+  p->fixed_opts.num_cus = cus;
+  p->caps.batch = max_batch;
+  p->caps.tokens = max_tokens;
+  p->caps.pages = max_pages;
+  fixed_capacities(p->Hkv, p->G, cus, &p->fixed_opts, &p->caps);
+  if (p->caps.partial_rows > INT32_MAX / 2 || p->caps.merges > INT32_MAX / 2) {
+    recycle_plan(p);
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: split workspace too large");
+  }
+  if (!host_only) {
+    const FixedLayout l = fixed_layout(p->caps, p->D);
+    hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    Workspace& w = p->ws;
+    w.device = dev;
+    hipError_t e = hipSuccess;
+    if (l.total > 0) e = hipMalloc(&w.dev, l.total);
+    if (e == hipSuccess && l.meta > 0) e = hipHostMalloc(&w.host, l.meta, hipHostMallocDefault);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
+    // every item and merge job starts as padding (zero rows, zero parts)
+    if (e == hipSuccess && l.meta > 0) e = hipMemsetAsync(w.dev, 0, l.meta, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      release_ws(w);
+      recycle_plan(p);
+      return e == hipErrorOutOfMemory ? fail(AK_ERR_OOM, "ak_plan_fixed: workspace")
+                                      : hip_fail(e, "ak_plan_fixed: workspace");
+    }
+    w.dev_bytes = l.total;
+    w.host_bytes = l.meta;
+    unsigned char* base = static_cast<unsigned char*>(w.dev);
+    p->d_buf = w.dev;
+    p->d_bytes = l.total;
+    p->d_reqs = reinterpret_cast<Req*>(base + l.req);
+    p->d_small = reinterpret_cast<Item*>(base + l.small);
+    p->d_large = reinterpret_cast<Item*>(base + l.large);
+    p->d_merges = reinterpret_cast<MergeJob*>(base + l.merge);
+    p->d_part_o = reinterpret_cast<float*>(base + l.po);
+    p->d_part_lse = reinterpret_cast<float*>(base + l.pl);
+  }
+  *plan = p;
+  return AK_OK;
+}
+
+extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
+                                    const int32_t* kv_indptr, const int32_t* last_page_len,
+                                    int32_t batch_size, void* stream) {
+  if (!plan) return fail(AK_ERR_INVALID_ARG, "ak_plan_update: null plan");
+  auto* p = static_cast<ak_plan_private*>(plan);
+  if (!p->fixed) return fail(AK_ERR_INVALID_ARG, "ak_plan_update: not a fixed plan");
+  if (batch_size > p->caps.batch) {
+    std::ostringstream os;
+    os << "ak_plan_update: batch_size " << batch_size << " exceeds the plan's " << p->caps.batch;
+    return fail(AK_ERR_SHAPE_MISMATCH, os.str());
+  }
+  ak_plan_private* t = new_plan();
+  if (!t) return fail(AK_ERR_OOM, "ak_plan_update: out of host memory");
+  ak_status st;
+  try {
+    st = build_plan_host(qo_indptr, kv_indptr, last_page_len, batch_size, p->Hq, p->Hkv, p->D, p->B,
+                         p->causal, p->window, &p->fixed_opts, p->num_cus, t);
+  } catch (const std::bad_alloc&) {
+    st = fail(AK_ERR_OOM, "ak_plan_update: out of host memory");
+  }
+  if (st == AK_OK && (t->T > p->caps.tokens || t->num_kv_pages > p->caps.pages)) {
+    std::ostringstream os;
+    os << "ak_plan_update: " << t->T << " query tokens and " << t->num_kv_pages
+       << " pages exceed the plan's " << p->caps.tokens << " and " << p->caps.pages;
+    st = fail(AK_ERR_SHAPE_MISMATCH, os.str());
+  }
+  if (st == AK_OK && ((int64_t)t->small_items.size() > p->caps.small ||
+                      (int64_t)t->large_items.size() > p->caps.large ||
+                      (int64_t)t->merges.size() > p->caps.merges || t->partial_rows > p->caps.partial_rows))
+    st = fail(AK_ERR_UNSUPPORTED, "ak_plan_update: the batch's work list exceeds the fixed workspace "
+                                  "(KV lengths outside the guaranteed range)");
+  if (st != AK_OK) {
+    recycle_plan(t);
+    return st;
+  }
+  if (!p->host_only) {
+    const FixedLayout l = fixed_layout(p->caps, p->D);
+    Workspace& w = p->ws;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipEventSynchronize(w.done);   // the previous upload has left the staging buffer
+    unsigned char* h = static_cast<unsigned char*>(w.host);
+    unsigned char* d = static_cast<unsigned char*>(w.dev);
+    // live entries, then padding over what the previous update left behind
+    auto stage = [&](size_t off, const void* src, int64_t n, int64_t hw, size_t esz) {
+      const int64_t m = std::max(n, hw);
+      if (e != hipSuccess || m == 0) return;
+      if (n > 0) std::memcpy(h + off, src, (size_t)n * esz);
+      if (hw > n) std::memset(h + off + (size_t)n * esz, 0, (size_t)(hw - n) * esz);
+      e = hipMemcpyAsync(d + off, h + off, (size_t)m * esz, hipMemcpyHostToDevice, s);
+    };
+    stage(l.req, t->reqs.data(), (int64_t)t->reqs.size(), 0, sizeof(Req));
+    stage(l.small, t->small_items.data(), (int64_t)t->small_items.size(), p->hw_small, sizeof(Item));
+    stage(l.large, t->large_items.data(), (int64_t)t->large_items.size(), p->hw_large, sizeof(Item));
+    stage(l.merge, t->merges.data(), (int64_t)t->merges.size(), p->hw_merges, sizeof(MergeJob));
+    if (e == hipSuccess) e = hipEventRecord(w.done, s);
+    if (e != hipSuccess) {
+      recycle_plan(t);
+      return hip_fail(e, "ak_plan_update: upload");
+    }
+    p->hw_small = (int64_t)t->small_items.size();
+    p->hw_large = (int64_t)t->large_items.size();
+    p->hw_merges = (int64_t)t->merges.size();
+  }
+  p->R = t->R;
+  p->T = t->T;
+  p->num_kv_pages = t->num_kv_pages;
+  p->partial_rows = t->partial_rows;
+  p->split_units = t->split_units;
+  std::swap(p->kv_lens, t->kv_lens);
+  std::swap(p->reqs, t->reqs);
+  std::swap(p->small_items, t->small_items);
+  std::swap(p->large_items, t->large_items);
+  std::swap(p->merges, t->merges);
+  recycle_plan(t);
+  return AK_OK;
 }
 
 // --------------------------------------------------------------------- run
@@ -461,10 +657,12 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   if (q->ndim != 3 || out->ndim != 3 || k_cache->ndim != 4 || v_cache->ndim != 4 ||
       (lse && lse->ndim != 2))
     return fail(AK_ERR_INVALID_ARG, "ak_run: expected q/out [T,Hq,D], caches [P,B,Hkv,D], lse [T,Hq]");
-  if (q->shape[0] != p->T || q->shape[1] != p->Hq || q->shape[2] != p->D) {
+  // a fixed plan runs on its token capacity (rows past the live ones are untouched)
+  const int64_t T_run = p->fixed ? p->caps.tokens : p->T;
+  if (q->shape[0] != T_run || q->shape[1] != p->Hq || q->shape[2] != p->D) {
     std::ostringstream os;
     os << "ak_run: q is [" << q->shape[0] << "," << q->shape[1] << "," << q->shape[2]
-       << "] but the plan expects [" << p->T << "," << p->Hq << "," << p->D << "]";
+       << "] but the plan expects [" << T_run << "," << p->Hq << "," << p->D << "]";
     return fail(AK_ERR_SHAPE_MISMATCH, os.str());
   }
   for (int i = 0; i < 3; ++i)
@@ -474,7 +672,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
       return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: k_cache and v_cache shapes differ");
   if (k_cache->shape[1] != p->B || k_cache->shape[2] != p->Hkv || k_cache->shape[3] != p->D)
     return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: cache page size, KV heads or head_dim differ from the plan");
-  if (lse && (lse->shape[0] != p->T || lse->shape[1] != p->Hq))
+  if (lse && (lse->shape[0] != T_run || lse->shape[1] != p->Hq))
     return fail(AK_ERR_SHAPE_MISMATCH, "ak_run: lse shape differs from [T, Hq]");
   if (lse && lse->dtype != AK_F32) return fail(AK_ERR_UNSUPPORTED, "ak_run: lse must be float32");
   if (out->dtype != q->dtype) return fail(AK_ERR_UNSUPPORTED, "ak_run: out dtype must equal q dtype");
@@ -484,7 +682,12 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   const bool ok = (qd == AK_F32 && kd == AK_F32) ||
                   (qd == AK_BF16 && (kd == AK_BF16 || kd == AK_FP8_E4M3));
   if (!ok) return fail(AK_ERR_UNSUPPORTED, "ak_run: supported q/cache dtypes are f32/f32, bf16/bf16, bf16/fp8");
-  if (p->T == 0 || (p->small_items.empty() && p->large_items.empty())) return AK_OK;
+  // a fixed plan launches over its whole capacity, whatever the live batch, so
+  // that a captured graph stays valid for every later update
+  const int ns = p->fixed ? (int)p->caps.small : (int)p->small_items.size();
+  const int nl = p->fixed ? (int)p->caps.large : (int)p->large_items.size();
+  const int nm = p->fixed ? (int)p->caps.merges : (int)p->merges.size();
+  if (T_run == 0 || (ns == 0 && nl == 0)) return AK_OK;
   if (!q->data || !out->data || !k_cache->data || !v_cache->data)
     return fail(AK_ERR_INVALID_ARG, "ak_run: null data pointer");
   if (q->stride[2] != 1 || out->stride[2] != 1 || k_cache->stride[3] != 1 || v_cache->stride[3] != 1)
@@ -535,7 +738,6 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  const int ns = (int)p->small_items.size(), nl = (int)p->large_items.size();
   if (qd == AK_F32) {
     a.items = p->d_small;
     {
@@ -563,7 +765,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
     }
     if (e != hipSuccess) return hip_fail(e, "ak_run: small-tile attention");
   }
-  if (!p->merges.empty()) {
+  if (nm > 0) {
     MergeArgs m{};
     m.jobs = p->d_merges;
     m.part_o = p->d_part_o;
@@ -574,7 +776,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
     m.o_sh = a.o_sh;
     m.l_st = a.l_st;
     m.l_sh = a.l_sh;
-    m.n_jobs = (int32_t)p->merges.size();
+    m.n_jobs = nm;
     {
       ProfScope ps(3, s);
       e = launch_merge(m, p->D, qd, s);
@@ -583,7 +785,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   }
   // the plan's workspace may be recycled only after this run has finished
   const auto* pp = static_cast<const ak_plan_private*>(p);
-  if (pp->ws.done) {
+  if (pp->ws.done && !p->fixed) {
     e = hipEventRecord(pp->ws.done, s);
     if (e != hipSuccess) return hip_fail(e, "ak_run: event record");
   }
@@ -659,15 +861,19 @@ extern "C" const char* ak_last_error(void) { return g_err.c_str(); }
 
 extern "C" ak_status ak_plan_info(const ak_plan_t* p, int64_t* info, int32_t n) {
   if (!p || !info || n < 0) return fail(AK_ERR_INVALID_ARG, "ak_plan_info: null argument");
-  const int64_t v[8] = {p->R,
+  const int64_t v[12] = {p->R,
                         p->T,
                         (int64_t)(p->small_items.size() + p->large_items.size()),
                         (int64_t)p->small_items.size(),
                         (int64_t)p->large_items.size(),
                         p->split_units,
                         (int64_t)p->merges.size(),
-                        p->partial_rows};
-  for (int i = 0; i < n && i < 8; ++i) info[i] = v[i];
+                        p->partial_rows,
+                        p->caps.small,
+                        p->caps.large,
+                        p->caps.merges,
+                        p->caps.partial_rows};
+  for (int i = 0; i < n && i < 12; ++i) info[i] = v[i];
   return AK_OK;
 }
 

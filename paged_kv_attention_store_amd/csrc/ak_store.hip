@@ -131,6 +131,7 @@ __global__ __launch_bounds__(256) void fp8_to_bf16_kernel(const uint8_t* __restr
 }  // namespace
 
 hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   const int64_t n8 = n / 8;
   if (n8 <= 0) return hipSuccess;
   int64_t blocks = (n8 + 255) / 256;
@@ -140,6 +141,7 @@ hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hi
 }
 
 hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   const int64_t total = (int64_t)a.N * a.Hkv * (a.D >> 3);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 8192) blocks = 8192;
@@ -161,6 +163,7 @@ hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hip
 hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int32_t* kv_indices,
                                int32_t R, int32_t log2B, int64_t num_pages, int64_t* slots,
                                hipStream_t s) {
+  (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (R <= 0) return hipSuccess;
   dim3 grid(64, (unsigned)R);
   hipLaunchKernelGGL(gather_slots_kernel, grid, dim3(256), 0, s, reqs, kv_off, kv_indices, log2B,

@@ -43,3 +43,18 @@ def test_binding_struct_layout_matches_header():
     # ak_tensor: void* + 2*int32 + 4*int64 + 4*int64 + float (+ padding) = 88 bytes
     assert ctypes.sizeof(ak.AkTensor) == 88
     assert ctypes.sizeof(ak.AkPlanOpts) == 32
+
+
+def test_one_hip_runtime_per_process():
+    # torch loads its own HIP runtime by path; the binding must make libak share
+    # it whatever the import order, or kernels launch on a runtime without devices
+    import subprocess
+    import sys
+
+    code = ("import paged_kv_attention_store_amd, torch\n"
+            "libs = {l.split()[-1] for l in open('/proc/self/maps') if 'libamdhip64' in l}\n"
+            "print(len(libs))\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True,
+                       timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.strip().splitlines()[-1] == "1"
