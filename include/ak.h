@@ -108,16 +108,24 @@ ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v, const ak_tensor* s
  *
  * Defines ("vLLM attention backend", "From a 2-D block table to a CSR page
  * table"; checked against the page's worked example): request r owns the first
- * pages_r = ceil(L_r / B) entries of its block-table row, and
+ * pages_r = ceil(L_r / B) kernel pages of its block-table row, and
  *   kv_indptr[0] = 0,  kv_indptr[r + 1] = kv_indptr[r] + pages_r,
- *   kv_indices[kv_indptr[r] + k] = block_table[r][k]   for k < pages_r,
+ *   kv_indices[kv_indptr[r] + k] = block_table[r][k / ratio] * ratio + k % ratio
+ *                                  for k < pages_r,
  *   last_page_len[r] = L_r - (pages_r - 1) * B  (in [1, B]; 0 when L_r = 0).
+ * block_ratio = 1 copies the row.  block_ratio > 1 is the same page's "Hybrid
+ * KV and virtual kernel blocks": the table holds manager blocks of
+ * block_ratio * B tokens, and manager block b of a cache [P, ratio * B, Hkv, D]
+ * is kernel pages b * ratio .. b * ratio + ratio - 1 of that cache viewed as
+ * [P * ratio, B, Hkv, D] (the view ak_run then reads).
  *
- *   block_table    device int32 [batch_size, max_pages], row-major, rows
- *                  contiguous; entries past pages_r are never read.
+ *   block_table    device int32 [batch_size, max_blocks], row-major, rows
+ *                  contiguous; entries past the blocks that cover L_r are never
+ *                  read.
  *   seq_lens       device int32 [batch_size], the KV length L_r of each request
  *                  (this step's tokens included).  A length outside
- *                  [0, max_pages * B] is clamped into it (the row holds no more).
+ *                  [0, max_blocks * block_ratio * B] is clamped into it (the
+ *                  row holds no more).
  *   kv_indptr      device int32 [batch_size + 1], written.
  *   kv_indices     device int32 [capacity], written in [0, kv_indptr[batch_size]);
  *                  entries at or past `capacity` are dropped, so a caller that
@@ -127,10 +135,13 @@ ak_status ak_store_kv(const ak_tensor* k, const ak_tensor* v, const ak_tensor* s
  * Outputs are caller-owned; the result is the plain definition above, bit for
  * bit (integer work).  Page ids are copied unchecked.  Enqueued on `stream`,
  * no host synchronisation, no allocation.  Errors: AK_ERR_INVALID_ARG (null
- * pointer, batch_size < 0, page_size < 1, max_pages < 0, capacity < 0), AK_ERR_HIP.
- * batch_size = 0 writes kv_indptr[0] = 0 only. */
-ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_pages,
+ * pointer, batch_size < 0, page_size < 1, block_ratio < 1, max_blocks < 0,
+ * capacity < 0), AK_ERR_UNSUPPORTED (block_ratio * page_size > 2^20 or
+ * max_blocks * block_ratio > 2^31 - 1), AK_ERR_HIP.  batch_size = 0 writes
+ * kv_indptr[0] = 0 only. */
+ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_blocks,
                                   const int32_t* seq_lens, int32_t batch_size, int32_t page_size,
+                                  int32_t block_ratio,
                                   int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
                                   int32_t* last_page_len, void* stream);
 
@@ -142,7 +153,8 @@ ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_pages,
  * r are its last n_r positions, so token qo_indptr[r] + j has position
  * p = L_r - n_r + j and slot block_table[r][p / B] * B + p % B.
  *
- *   block_table   device int32 [batch_size, max_pages], as above.
+ *   block_table   device int32 [batch_size, max_pages], as above (with manager
+ *                 blocks, pass their size as page_size: the slot is the same).
  *   qo_indptr     device int32 [batch_size + 1], starting at 0, non-decreasing.
  *   seq_lens      device int32 [batch_size], L_r with this step's tokens.
  *   slot_mapping  device int64 [num_tokens], written: the slot, or -1 for a

@@ -42,6 +42,20 @@ def block_table_to_csr(seq_lens, block_rows, page_size):
             np.asarray(last, dtype=np.int64))
 
 
+def virtual_block_rows(block_rows, ratio):
+    """Manager-block rows -> kernel-page rows.
+
+    A manager block of M = ratio * B tokens is exposed to a kernel that takes
+    B-token pages as `ratio` virtual kernel blocks; the expansion has to agree
+    with the cache view, so block b of a cache [P, M, Hkv, D] becomes pages
+    b * ratio + i (i < ratio) of the same memory viewed as [P * ratio, B, Hkv, D].
+    [vLLM backend, "Hybrid KV and virtual kernel blocks"; the formula is the
+    reading that keeps every flat slot unchanged]
+    """
+    ratio = int(ratio)
+    return [[int(b) * ratio + i for b in row for i in range(ratio)] for row in block_rows]
+
+
 def kv_lengths(kv_indptr, last_page_len, page_size):
     """CSR page table -> KV length of every request.
 

@@ -103,8 +103,8 @@ def _load():
     lib.ak_merge_states.argtypes = [P(AkTensor)] * 6 + [ctypes.c_void_p]
     lib.ak_merge_states.restype = ctypes.c_int
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
-    lib.ak_csr_from_block_table.argtypes = [vp, i64, vp, ctypes.c_int32, ctypes.c_int32, vp, vp,
-                                            i64, vp, vp]
+    lib.ak_csr_from_block_table.argtypes = [vp, i64, vp, ctypes.c_int32, ctypes.c_int32,
+                                            ctypes.c_int32, vp, vp, i64, vp, vp]
     lib.ak_csr_from_block_table.restype = ctypes.c_int
     lib.ak_slot_mapping.argtypes = [vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
     lib.ak_slot_mapping.restype = ctypes.c_int
@@ -380,14 +380,16 @@ def _torch():
 
 
 def ak_csr_from_block_table(block_table, seq_lens, page_size: int, kv_indices=None,
-                            kv_indptr=None, last_page_len=None, stream=None):
+                            kv_indptr=None, last_page_len=None, block_ratio: int = 1, stream=None):
     """Build (kv_indptr, kv_indices, last_page_len) from a device block table
-    [R, max_pages] and device seq_lens [R] (all int32).  kv_indices defaults to
-    R * max_pages entries, enough for any lengths; the valid prefix is
+    [R, max_blocks] and device seq_lens [R] (all int32).  With block_ratio > 1 the
+    table holds manager blocks of block_ratio * page_size tokens and the CSR lists
+    page_size-token kernel pages.  kv_indices defaults to R * max_blocks *
+    block_ratio entries, enough for any lengths; the valid prefix is
     kv_indices[:kv_indptr[R]]."""
     torch = _torch()
     _dev_i32_matrix(block_table, "block_table")
-    R, max_pages = block_table.shape
+    R, max_blocks = block_table.shape
     _dev_i32_vector(seq_lens, R, "seq_lens")
     dev = block_table.device
     if kv_indptr is None:
@@ -395,13 +397,14 @@ def ak_csr_from_block_table(block_table, seq_lens, page_size: int, kv_indices=No
     if last_page_len is None:
         last_page_len = torch.empty(R, dtype=torch.int32, device=dev)
     if kv_indices is None:
-        kv_indices = torch.empty(max(R * max_pages, 1), dtype=torch.int32, device=dev)
+        kv_indices = torch.empty(max(R * max_blocks * int(block_ratio), 1), dtype=torch.int32,
+                                 device=dev)
     _dev_i32_vector(kv_indptr, R + 1, "kv_indptr")
     _dev_i32_vector(last_page_len, R, "last_page_len")
     _dev_i32_vector(kv_indices, 0, "kv_indices")
     _check(_lib.ak_csr_from_block_table(
-        ctypes.c_void_p(block_table.data_ptr()), max_pages, ctypes.c_void_p(seq_lens.data_ptr()),
-        R, int(page_size), ctypes.c_void_p(kv_indptr.data_ptr()),
+        ctypes.c_void_p(block_table.data_ptr()), max_blocks, ctypes.c_void_p(seq_lens.data_ptr()),
+        R, int(page_size), int(block_ratio), ctypes.c_void_p(kv_indptr.data_ptr()),
         ctypes.c_void_p(kv_indices.data_ptr()), kv_indices.numel(),
         ctypes.c_void_p(last_page_len.data_ptr()), _stream_ptr(stream)))
     return kv_indptr, kv_indices, last_page_len

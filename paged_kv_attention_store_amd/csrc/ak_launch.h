@@ -36,7 +36,7 @@ hipError_t launch_attn_f32(const AttnArgs& a, int n_items, int D, hipStream_t s)
 hipError_t launch_merge(const MergeArgs& a, int D, int out_dtype, hipStream_t s);
 hipError_t launch_merge2(const Merge2Args& a, int D, int dtype, hipStream_t s);
 hipError_t launch_csr_from_block_table(const int32_t* block_table, int64_t row_stride,
-                                       const int32_t* seq_lens, int32_t R, int32_t B,
+                                       const int32_t* seq_lens, int32_t R, int32_t B, int32_t ratio,
                                        int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
                                        int32_t* last_page_len, hipStream_t s);
 hipError_t launch_slot_mapping(const int32_t* block_table, int64_t row_stride, const int32_t* qo_indptr,

@@ -8,6 +8,11 @@
 // page and "Write the KV first": token j of the n_r new tokens of request r sits
 // at position p = L_r - n_r + j and is written to slot page[p / B] * B + p % B.
 //
+// "vLLM attention backend", "Hybrid KV and virtual kernel blocks": when the
+// cache manager's block holds M = ratio * B tokens and the kernel takes B-token
+// pages, manager block b is kernel pages b * ratio .. b * ratio + ratio - 1 of the
+// same cache viewed as [P * ratio, B, Hkv, D]; the CSR lists kernel pages.
+//
 // Integer work only.  The running sum is one workgroup (the batch is at most a
 // few thousand requests); the copy of page ids and the slot computation are
 // spread over the machine.
@@ -20,9 +25,9 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 
-// a length is clamped into [0, row_stride * B] so that its pages stay inside the row
-__device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t B, int64_t row_stride) {
-  const int64_t cap = row_stride * (int64_t)B;
+// a length is clamped into [0, row_stride * ratio * B] so that its pages stay inside the row
+__device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t B, int64_t row_stride, int32_t ratio) {
+  const int64_t cap = row_stride * ratio * (int64_t)B;
   return L <= 0 ? 0 : (int32_t)((int64_t)L < cap ? (int64_t)L : cap);
 }
 
@@ -31,6 +36,7 @@ __device__ __forceinline__ int32_t clamp_len(int32_t L, int32_t B, int64_t row_s
 // the running carry of the chunks before it
 __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* __restrict__ seq_lens,
                                                                 int32_t R, int32_t B, int64_t row_stride,
+                                                                int32_t ratio,
                                                                 int32_t* __restrict__ kv_indptr,
                                                                 int32_t* __restrict__ last_page_len) {
   __shared__ int32_t wsum[kScanThreads / 64];
@@ -43,7 +49,7 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* _
   __syncthreads();
   for (int32_t base = 0; base < R; base += kScanThreads) {
     const int32_t r = base + tid;
-    const int32_t L = r < R ? clamp_len(seq_lens[r], B, row_stride) : 0;
+    const int32_t L = r < R ? clamp_len(seq_lens[r], B, row_stride, ratio) : 0;
     const int32_t pg = (int32_t)(((int64_t)L + B - 1) / B);
     int32_t v = pg;
 #pragma unroll
@@ -66,17 +72,22 @@ __global__ __launch_bounds__(kScanThreads) void csr_scan_kernel(const int32_t* _
   }
 }
 
-// kv_indices: workgroup r copies the page ids of request r
+// kv_indices: workgroup r writes the kernel pages of request r
 __global__ __launch_bounds__(256) void csr_copy_kernel(const int32_t* __restrict__ block_table,
-                                                       int64_t row_stride,
+                                                       int64_t row_stride, int32_t ratio,
                                                        const int32_t* __restrict__ kv_indptr,
                                                        int32_t* __restrict__ kv_indices,
                                                        int64_t capacity) {
   const int32_t r = blockIdx.x;
   const int64_t a = kv_indptr[r], b = kv_indptr[r + 1];
   const int32_t* row = block_table + (int64_t)r * row_stride;
-  for (int64_t i = threadIdx.x; i < b - a; i += 256)
-    if (a + i < capacity) kv_indices[a + i] = row[i];
+  if (ratio == 1) {
+    for (int64_t i = threadIdx.x; i < b - a; i += 256)
+      if (a + i < capacity) kv_indices[a + i] = row[i];
+  } else {
+    for (int64_t i = threadIdx.x; i < b - a; i += 256)
+      if (a + i < capacity) kv_indices[a + i] = row[i / ratio] * ratio + (int32_t)(i % ratio);
+  }
 }
 
 // slot_mapping: one thread per new token; its request by binary search in qo_indptr
@@ -106,16 +117,16 @@ __global__ __launch_bounds__(256) void slots_kernel(const int32_t* __restrict__ 
 }  // namespace
 
 hipError_t launch_csr_from_block_table(const int32_t* block_table, int64_t row_stride,
-                                       const int32_t* seq_lens, int32_t R, int32_t B,
+                                       const int32_t* seq_lens, int32_t R, int32_t B, int32_t ratio,
                                        int32_t* kv_indptr, int32_t* kv_indices, int64_t capacity,
                                        int32_t* last_page_len, hipStream_t s) {
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, seq_lens, R, B, row_stride,
-                     kv_indptr, last_page_len);
+                     ratio, kv_indptr, last_page_len);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || R == 0) return e;
   hipLaunchKernelGGL(csr_copy_kernel, dim3((unsigned)R), dim3(256), 0, s, block_table, row_stride,
-                     kv_indptr, kv_indices, capacity);
+                     ratio, kv_indptr, kv_indices, capacity);
   return hipGetLastError();
 }
 

@@ -919,18 +919,21 @@ extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* s
   return AK_OK;
 }
 
-extern "C" ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_pages,
+extern "C" ak_status ak_csr_from_block_table(const int32_t* block_table, int64_t max_blocks,
                                              const int32_t* seq_lens, int32_t batch_size,
-                                             int32_t page_size, int32_t* kv_indptr,
+                                             int32_t page_size, int32_t block_ratio, int32_t* kv_indptr,
                                              int32_t* kv_indices, int64_t capacity,
                                              int32_t* last_page_len, void* stream) {
-  if (batch_size < 0 || page_size < 1 || max_pages < 0 || capacity < 0)
-    return fail(AK_ERR_INVALID_ARG, "ak_csr_from_block_table: negative size or page_size < 1");
+  if (batch_size < 0 || page_size < 1 || max_blocks < 0 || capacity < 0 || block_ratio < 1)
+    return fail(AK_ERR_INVALID_ARG,
+                "ak_csr_from_block_table: negative size, page_size < 1 or block_ratio < 1");
+  if ((int64_t)page_size * block_ratio > (1 << 20) || max_blocks * block_ratio > INT32_MAX)
+    return fail(AK_ERR_UNSUPPORTED, "ak_csr_from_block_table: block too large");
   if (!kv_indptr || (batch_size > 0 && (!block_table || !seq_lens || !last_page_len)) ||
       (capacity > 0 && !kv_indices))
     return fail(AK_ERR_INVALID_ARG, "ak_csr_from_block_table: null pointer");
-  hipError_t e = launch_csr_from_block_table(block_table, max_pages, seq_lens, batch_size, page_size,
-                                             kv_indptr, kv_indices, capacity, last_page_len,
+  hipError_t e = launch_csr_from_block_table(block_table, max_blocks, seq_lens, batch_size, page_size,
+                                             block_ratio, kv_indptr, kv_indices, capacity, last_page_len,
                                              static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(e, "ak_csr_from_block_table");
   return AK_OK;

@@ -103,6 +103,44 @@ def test_csr_and_slots_bit_exact(R, B, max_pages, seed):
     assert np.all(got[qo[-1]:] == -1)
 
 
+@pytest.mark.parametrize("ratio,B", [(2, 16), (4, 16), (8, 8), (3, 32)])
+def test_csr_virtual_blocks_bit_exact(ratio, B):
+    rng = np.random.default_rng(ratio * B)
+    R, mb = 300, 20
+    Mtok = ratio * B
+    L = rng.integers(0, mb * Mtok + 1, size=R)
+    L[::17] = 0
+    L[5] = mb * Mtok
+    rows = [rng.integers(0, 5000, size=-(-int(l) // Mtok)) for l in L]
+    table = _table(rows, mb, rng)
+    bt = torch.from_numpy(table).cuda()
+    ip, ix, lp = ak.ak_csr_from_block_table(bt, torch.from_numpy(L.astype(np.int32)).cuda(), B,
+                                            block_ratio=ratio)
+    torch.cuda.synchronize()
+    ip, ix, lp = ip.cpu().numpy(), ix.cpu().numpy(), lp.cpu().numpy()
+    ei, ex, el = M.block_table_to_csr(L, M.virtual_block_rows(rows, ratio), B)
+    assert np.array_equal(ip, ei) and np.array_equal(ix[:ip[-1]], ex) and np.array_equal(lp, el)
+
+
+def test_attention_through_virtual_kernel_blocks():
+    # the cache is managed in 64-token blocks; the kernels read it as 16-token pages
+    wl = W.custom(seed=41, q_lens=[1, 1, 20, 1], kv_lens=[700, 64, 300, 1], page_size=64,
+                  num_qo_heads=32, num_kv_heads=8, head_dim=128, name="virtual_blocks")
+    say("[metadata] 64-token manager blocks as 16-token kernel pages")
+    d = prepare(wl)
+    ratio, B = 4, 16
+    table = _table(wl.req_pages, max(len(p) for p in wl.req_pages))
+    sl = torch.from_numpy(wl.kv_lens.astype(np.int32)).cuda()
+    ip, ix, lp = ak.ak_csr_from_block_table(torch.from_numpy(table).cuda(), sl, B, block_ratio=ratio)
+    P = wl.num_pages
+    kc = d["k_cache"].view(P * ratio, B, 8, 128)
+    vc = d["v_cache"].view(P * ratio, B, 8, 128)
+    plan = ak.ak_plan(wl.qo_indptr, ip.cpu().numpy(), ix, lp.cpu().numpy(), 32, 8, 128, B)
+    out, lse = ak.ak_run(plan, d["q"], kc, vc, lse=torch.empty(wl.total_q, 32, device="cuda"))
+    torch.cuda.synchronize()
+    check(wl, out, lse, -1)
+
+
 def test_csr_capacity_and_clamped_lengths():
     rng = np.random.default_rng(11)
     R, B, mp = 50, 16, 6

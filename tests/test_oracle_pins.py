@@ -65,6 +65,37 @@ def test_vllm_worked_example_slices_cover_every_token_once():
     assert sorted(covered) == list(range(int(qsl[-1])))
 
 
+def test_virtual_blocks_of_the_pages_example():
+    # a 64-token manager block seen as four 16-token kernel blocks: manager
+    # blocks 5 and 2 are kernel pages 20..23 and 8..11 of the 16-token view
+    assert M.virtual_block_rows([[5, 2]], 4) == [[20, 21, 22, 23, 8, 9, 10, 11]]
+    assert M.virtual_block_rows([[7, 0, 3]], 1) == [[7, 0, 3]]
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 4, 8])
+def test_virtual_blocks_keep_every_flat_slot(ratio):
+    # the expansion is a relabelling of one memory: position p of a request has
+    # the same flat slot through M-token manager blocks and B-token kernel pages
+    # (slot_of is pinned by the vLLM worked example)
+    rng = np.random.default_rng(ratio)
+    B = 16
+    Mtok = ratio * B
+    rows = [rng.permutation(50)[:k].tolist() for k in (1, 3, 7)]
+    vrows = M.virtual_block_rows(rows, ratio)
+    for row, vrow in zip(rows, vrows):
+        L = len(row) * Mtok
+        for p in range(L):
+            assert M.slot_of(row, p, Mtok) == M.slot_of(vrow, p, B)
+    # and the CSR built from kernel pages gathers the same slots as the one built
+    # from manager blocks
+    lens = [5, 3 * Mtok - 1, 7 * Mtok]
+    i1, x1, l1 = M.block_table_to_csr(lens, rows, Mtok)
+    i2, x2, l2 = M.block_table_to_csr(lens, vrows, B)
+    for r in range(3):
+        assert np.array_equal(M.request_slots(i1, x1, l1, Mtok, r),
+                              M.request_slots(i2, x2, l2, B, r))
+
+
 def test_last_page_len_never_zero():
     # a full last page is B, not 0 (CSR section of the vLLM page)
     for B in (1, 2, 16, 64):
