@@ -11,13 +11,16 @@ inputs are resident in HBM before the timed region.
 bytes per layer = visible KV rows (K and V) + Q + out + lse + page ids read,
 plus the store's reads and writes.  The roofline object reports the decode
 attention kernel alone: its algorithmic bytes per launch over its average
-duration from HIP events recorded around every launch on the launch stream.
+duration from HIP events recorded, during the timed steps, around every launch
+of that kernel on the launch stream (only the attention kernels carry events in
+the timed steps; store and merge times come from a separate detail pass).
 
 Further workloads (--also) are reported under their names: the ragged extend
 batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
 the mixed chunked-prefill + decode step with full and sliding-window layers
-("mixed"), the fp8 long-context decode ("longfp8"), and decode requests sharing
-a 4096-token prefix run plainly and as a cascade ("cascade").
+("mixed"), the fp8 long-context decode ("longfp8"), decode requests sharing
+a 4096-token prefix run plainly and as a cascade ("cascade"), and a small
+decode batch issued eagerly and as a replayed graph over a fixed plan ("graph").
 
 The CPU baseline times the float64 oracle on a sample of the decode batch.
 """
@@ -193,8 +196,14 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     torch.cuda.synchronize()
     run_steps(ak, wl, layers, idx, slots, warmup)
     torch.cuda.synchronize()
+    # the timed steps carry HIP events around the attention kernels only (each
+    # event pair adds a few microseconds between kernels); the store and merge
+    # are timed in a separate detail pass
+    G = wl.num_qo_heads // wl.num_kv_heads
+    kinds = (["attn_small"] if np.any(wl.q_lens * G <= 16) else []) + \
+            (["attn_large"] if np.any(wl.q_lens * G > 16) else [])
     ak.ak_profile_read()                      # reset counters
-    ak.ak_profile_enable(True)
+    ak.ak_profile_enable(True, kinds=kinds)
     t0 = time.perf_counter()
     plan_s, plans = run_steps(ak, wl, layers, idx, slots, steps)
     torch.cuda.synchronize()
@@ -202,6 +211,12 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     ak.ak_profile_enable(False)
     prof = ak.ak_profile_read()
     ms_step = (t1 - t0) * 1e3 / steps
+    detail_steps = max(2, steps // 2)
+    ak.ak_profile_enable(True, kinds=["store_kv", "merge"])
+    run_steps(ak, wl, layers, idx, slots, detail_steps)
+    torch.cuda.synchronize()
+    ak.ak_profile_enable(False)
+    detail = ak.ak_profile_read()
     # host cost of planning alone (the in-loop figure also holds any wait for a
     # free workspace when the host runs ahead of the GPU)
     t = time.perf_counter()
@@ -228,11 +243,11 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     if n and flops:
         res["large_avg_ms"] = ms / n
         res["large_tflops"] = flops * steps / (ms * 1e-3) / 1e12
-    n, ms = prof["store_kv"]
+    n, ms = detail["store_kv"]
     if n:
         res["store_avg_us"] = ms / n * 1e3
         res["store_gbs"] = store_bytes(wl) / (ms / n * 1e-3) / 1e9
-    n, ms = prof["merge"]
+    n, ms = detail["merge"]
     if n:
         res["merge_avg_us"] = ms / n * 1e3
     msg = (f"[bench] {wl.name}: {ms_step:.3f} ms/step, step-level {res['gbs']:.1f} GB/s; "
@@ -241,7 +256,7 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
         msg += f"attn_small {res['small_avg_ms'] * 1e3:.1f} us -> {res['small_gbs']:.1f} GB/s; "
     if "large_tflops" in res:
         msg += f"attn_large {res['large_avg_ms'] * 1e3:.1f} us -> {res['large_tflops']:.1f} TFLOP/s; "
-    log(msg + f"profile {prof}; plan {res['info']}")
+    log(msg + f"profile {prof}; detail {detail}; plan {res['info']}")
     del layers
     torch.cuda.empty_cache()
     return res
@@ -368,12 +383,81 @@ def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
     return res
 
 
+def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup):
+    """Small-batch decode, where launch cost dominates: the same step (plan, then
+    store_kv + run per layer) issued eagerly, and as a fixed plan updated on the
+    host plus one replay of a graph holding every layer's store and run.  Wall
+    time per step (host and device), the step's outputs compared bit for bit."""
+    log(f"[bench] {wl.name}: R={wl.batch_size} KV tokens={int(wl.kv_lens.sum())} "
+        f"layers={n_layers} (eager vs graph replay)")
+    layers = make_layers(wl, n_layers, dev)
+    idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
+    slots = torch.from_numpy(wl.slot_mapping).to(dev)
+    hq, hkv, D, B = wl.num_qo_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
+
+    def eager_step():
+        plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B)
+        for L in layers:
+            ak.ak_store_kv(L["kn"], L["vn"], slots, L["kc"], L["vc"])
+            ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+
+    fixed = ak.ak_plan_fixed(wl.batch_size, wl.total_q, idx, hq, hkv, D, B,
+                             max_query_len=int(wl.q_lens.max()), merge_in_kernel=True)
+    ak.ak_plan_update(fixed, wl.qo_indptr, wl.kv_indptr, wl.last_page_len)
+
+    def body():
+        for L in layers:
+            ak.ak_store_kv(L["kn"], L["vn"], slots, L["kc"], L["vc"])
+            ak.ak_run(fixed, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+
+    body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+
+    def graph_step():
+        ak.ak_plan_update(fixed, wl.qo_indptr, wl.kv_indptr, wl.last_page_len)
+        g.replay()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps
+
+    eager_us, graph_us = timed(eager_step), timed(graph_step)
+    eager_step()
+    torch.cuda.synchronize()
+    ref = [L["out"].clone() for L in layers]
+    graph_step()
+    torch.cuda.synchronize()
+    same = all(torch.equal(r, L["out"]) for r, L in zip(ref, layers))
+    step_bytes = n_layers * (decode_bytes(wl) + store_bytes(wl))
+    res = {"workload": wl.name, "layers": n_layers, "requests": wl.batch_size,
+           "kv_tokens": int(wl.kv_lens.sum()), "eager_us_per_step": round(eager_us, 1),
+           "graph_us_per_step": round(graph_us, 1), "speedup": round(eager_us / graph_us, 2),
+           "graph_step_GBs": round(step_bytes / (graph_us * 1e-6) / 1e9, 1),
+           "outputs_identical": bool(same), "capacity": {k: v for k, v in fixed.info().items()
+                                                         if k.startswith("cap_")}}
+    log(f"[bench] {wl.name}: eager {eager_us:.1f} us/step, graph {graph_us:.1f} us/step "
+        f"(x{res['speedup']}, {res['graph_step_GBs']} GB/s step-level), identical={same}")
+    del layers, g
+    torch.cuda.empty_cache()
+    return res
+
+
 WORKLOADS = {
     # name: (factory, layers with distinct caches)
     "prefill": (lambda W: W.config(3), 2),
     "mixed": (lambda W: W.config(4), 4),
     "longfp8": (lambda W: W.config(5), 4),
     "cascade": (lambda W: W.shared_prefix_decode(), 8),
+    "graph": (lambda W: W.small_batch_decode(), 32),
 }
 
 
@@ -384,7 +468,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
     ap.add_argument("--also", default="prefill",
-                    help="comma list of further workloads: prefill,mixed,longfp8 ('' for none)")
+                    help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph "
+                         "('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy timed as bandwidth context (0: skip)")
@@ -407,6 +492,9 @@ def main():
         fac, nl = WORKLOADS[name]
         if name == "cascade":
             extra[name] = measure_cascade(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
+            continue
+        if name == "graph":
+            extra[name] = measure_graph(ak, torch, dev, fac(W), nl, max(5, args.steps), 3)
             continue
         extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
@@ -451,7 +539,7 @@ def main():
         "copy_GBs": copy,
     }
     for name, r in extra.items():
-        if name == "cascade":
+        if name in ("cascade", "graph"):
             line[name] = r
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),

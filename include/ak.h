@@ -173,7 +173,13 @@ ak_status ak_slot_mapping(const int32_t* block_table, int64_t max_pages, const i
 
 typedef struct ak_plan_t ak_plan_t;    /* opaque; owned by the library */
 
-enum { AK_PLAN_HOST_ONLY = 1 };        /* build the work list without touching the GPU */
+enum {
+  AK_PLAN_HOST_ONLY = 1,        /* build the work list without touching the GPU           */
+  AK_PLAN_MERGE_IN_KERNEL = 2   /* split decode units (<= 16 rows) are merged by the last of
+                                   their parts inside the attention kernel (bf16 q) instead
+                                   of by a separate merge launch: one launch fewer per run,
+                                   for launch-bound small batches; slower for large ones  */
+};
 
 typedef struct {
   float sm_scale;        /* softmax scale; <= 0 selects 1/sqrt(head_dim)            */
@@ -183,7 +189,7 @@ typedef struct {
                             only when a split would span more than 1024 pages (page
                             size 1 or 2 with long contexts)                        */
   int32_t min_chunk;     /* smallest KV split in tokens; 0 = library default       */
-  int32_t flags;         /* AK_PLAN_HOST_ONLY                                       */
+  int32_t flags;         /* AK_PLAN_HOST_ONLY | AK_PLAN_MERGE_IN_KERNEL              */
   void* stream;          /* stream for the plan's upload; NULL = default stream     */
 } ak_plan_opts;
 
@@ -313,7 +319,10 @@ ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak
  * persistent scheduling metadata cleared so that stale entries write nothing).
  *
  * ak_plan_fixed allocates, once, a workspace sized for any batch of at most
- * max_batch requests, max_tokens query tokens and max_pages pages: the work list
+ * max_batch requests, max_tokens query tokens, max_query_len query tokens in any
+ * one request (0 = max_tokens; 1 for pure decode, where max_query_len *
+ * num_qo_heads / num_kv_heads <= 16 also drops the large-tile launch) and
+ * max_pages pages: the work list
  * with room for every split the planner may choose, the split partials and the
  * merge list, all zeroed (a zero entry is padding: its workgroup exits at once).
  * Geometry (heads, head_dim, page_size, causal, window) and opts are fixed with
@@ -342,8 +351,8 @@ ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak
  * the capacities), AK_ERR_BAD_INDPTR / AK_ERR_BAD_LENGTHS (as ak_plan),
  * AK_ERR_OOM, AK_ERR_HIP.  With AK_PLAN_HOST_ONLY in opts->flags nothing is
  * allocated or uploaded (for checking the work list and capacities). */
-ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_pages,
-                        const int32_t* kv_indices, int32_t num_qo_heads, int32_t num_kv_heads,
+ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_query_len,
+                        int64_t max_pages, const int32_t* kv_indices, int32_t num_qo_heads, int32_t num_kv_heads,
                         int32_t head_dim, int32_t page_size, int32_t causal, int32_t window,
                         const ak_plan_opts* opts, ak_plan_t** plan);
 ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
@@ -387,12 +396,17 @@ ak_status ak_gather_slots(const ak_plan_t* plan, int64_t* slots, void* stream);
 ak_status ak_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, void* stream);
 
 /* Per-kernel timing with HIP events on the launch stream (diagnostics).
- * ak_profile_enable(1) records an event pair around every kernel the library
- * launches; ak_profile_read copies, per kernel kind (0 store, 1 small-tile
- * attention, 2 large-tile attention, 3 merge, 4 fp32 attention), the launch
- * count and the summed milliseconds measured so far into host arrays of
- * length n, then resets the counters.  Reading synchronises on the events. */
-ak_status ak_profile_enable(int32_t on);
+ * Kernel kinds: 0 store, 1 small-tile attention, 2 large-tile attention,
+ * 3 merge, 4 fp32 attention.  ak_profile_enable(kinds) records an event pair
+ * around every launch of the kinds whose bit (1 << kind) is set in `kinds`
+ * (0 = off; AK_PROFILE_ALL = every kind; launches during stream capture are
+ * never timed).  Each pair adds a few microseconds between kernels, so time
+ * only the kinds needed.  ak_profile_read copies, per kind, the launch count and
+ * the summed milliseconds measured so far into host arrays of length n, then
+ * resets the counters.  Reading synchronises on the events.
+ * Errors: AK_ERR_INVALID_ARG (negative mask). */
+enum { AK_PROFILE_ALL = 0x1F };
+ak_status ak_profile_enable(int32_t kinds);
 ak_status ak_profile_read(int64_t* launches, double* total_ms, int32_t n);
 
 /* Library version string. */

@@ -41,6 +41,8 @@ STATUS_NAMES = {0: "AK_OK", -1: "AK_ERR_INVALID_ARG", -2: "AK_ERR_UNSUPPORTED",
 
 AK_F32, AK_BF16, AK_FP8_E4M3, AK_I32, AK_I64 = 0, 1, 2, 3, 4
 AK_PLAN_HOST_ONLY = 1
+AK_PLAN_MERGE_IN_KERNEL = 2
+AK_PROFILE_ALL = 0x1F
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
@@ -85,7 +87,8 @@ def _load():
     lib.ak_plan.argtypes = [i32p, i32p, ctypes.c_void_p, i32p] + [ctypes.c_int32] * 7 + [
         P(AkPlanOpts), P(ctypes.c_void_p)]
     lib.ak_plan.restype = ctypes.c_int
-    lib.ak_plan_fixed.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p] + [
+    lib.ak_plan_fixed.argtypes = [ctypes.c_int32, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                  ctypes.c_void_p] + [
         ctypes.c_int32] * 6 + [P(AkPlanOpts), P(ctypes.c_void_p)]
     lib.ak_plan_fixed.restype = ctypes.c_int
     lib.ak_plan_update.argtypes = [ctypes.c_void_p, i32p, i32p, i32p, ctypes.c_int32, ctypes.c_void_p]
@@ -207,7 +210,9 @@ class Plan:
         self._keep = keep           # the borrowed kv_indices tensor stays alive with the plan
 
     def __del__(self):
-        ak_plan_destroy(self)
+        destroy = globals().get("ak_plan_destroy")
+        if destroy is not None:         # None while the interpreter shuts down
+            destroy(self)
 
     def info(self) -> dict:
         return ak_plan_info(self)
@@ -216,7 +221,8 @@ class Plan:
 def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, num_kv_heads: int,
             head_dim: int, page_size: int, causal: bool = True, window: int = -1,
             sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
-            min_chunk: int = 0, host_only: bool = False, stream=None) -> Plan:
+            min_chunk: int = 0, host_only: bool = False, merge_in_kernel: bool = False,
+            stream=None) -> Plan:
     """Build a plan.  qo_indptr, kv_indptr and last_page_len are host arrays
     (anything NumPy accepts); kv_indices is a device int32 tensor (or None for a
     host-only plan)."""
@@ -231,7 +237,8 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
     opts.num_cus = int(num_cus)
     opts.max_splits = int(max_splits)
     opts.min_chunk = int(min_chunk)
-    opts.flags = AK_PLAN_HOST_ONLY if host_only else 0
+    opts.flags = (AK_PLAN_HOST_ONLY if host_only else 0) | (
+        AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0)
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None:
@@ -252,16 +259,19 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
                   num_kv_heads: int, head_dim: int, page_size: int, causal: bool = True,
                   window: int = -1, sm_scale: float | None = None, num_cus: int = 0,
                   max_splits: int = 0, min_chunk: int = 0, host_only: bool = False,
-                  max_pages: int | None = None, stream=None) -> Plan:
+                  max_pages: int | None = None, max_query_len: int = 0,
+                  merge_in_kernel: bool = False, stream=None) -> Plan:
     """A plan with a fixed device workspace for graph capture.  kv_indices is the
     stable device int32 buffer later batches write their page ids into (its size
-    is the page capacity); host-only plans take None and max_pages."""
+    is the page capacity); host-only plans take None and max_pages.  max_query_len
+    bounds any one request's query tokens (0 = max_tokens; 1 for pure decode)."""
     opts = AkPlanOpts()
     opts.sm_scale = float(sm_scale) if sm_scale else 0.0
     opts.num_cus = int(num_cus)
     opts.max_splits = int(max_splits)
     opts.min_chunk = int(min_chunk)
-    opts.flags = AK_PLAN_HOST_ONLY if host_only else 0
+    opts.flags = (AK_PLAN_HOST_ONLY if host_only else 0) | (
+        AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0)
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None and not host_only:
@@ -273,7 +283,8 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
         if max_pages is None:
             max_pages = kv_indices.numel()
     h = ctypes.c_void_p()
-    _check(_lib.ak_plan_fixed(int(max_batch), int(max_tokens), int(max_pages or 0), idx_ptr,
+    _check(_lib.ak_plan_fixed(int(max_batch), int(max_tokens), int(max_query_len),
+                              int(max_pages or 0), idx_ptr,
                               num_qo_heads, num_kv_heads, head_dim, page_size, int(bool(causal)),
                               int(window), ctypes.byref(opts), ctypes.byref(h)))
     plan = Plan(h, num_qo_heads, num_kv_heads, head_dim, page_size, host_only, kv_indices)
@@ -436,8 +447,13 @@ def ak_slot_mapping(block_table, qo_indptr, seq_lens, page_size: int, num_tokens
 KERNEL_KINDS = ["store_kv", "attn_small", "attn_large", "merge", "attn_f32"]
 
 
-def ak_profile_enable(on: bool = True) -> None:
-    _check(_lib.ak_profile_enable(int(bool(on))))
+def ak_profile_enable(on: bool = True, kinds=None) -> None:
+    """Time launches with HIP events: every kernel kind, or only the named ones
+    (names from KERNEL_KINDS)."""
+    mask = 0
+    if on:
+        mask = AK_PROFILE_ALL if kinds is None else sum(1 << KERNEL_KINDS.index(k) for k in kinds)
+    _check(_lib.ak_profile_enable(mask))
 
 
 def ak_profile_read() -> dict:

@@ -74,6 +74,24 @@ struct Shape {
   static constexpr int STAGE = BLK * VROW;                      // bf16 elements per wave stage
 };
 
+// s_waitcnt operand that waits for every outstanding vector memory operation
+// (vmcnt 0; expcnt and lgkmcnt left at their maxima)
+constexpr int kVmcntZero = 0x0F70;
+
+// CPT consecutive fp32 values of one output row as bf16 (8 or 4 columns: one
+// 16- or 8-byte store)
+template <int CPT>
+__device__ __forceinline__ void store_row_bf16(uint16_t* op, const float* o) {
+  u32x4 w4;
+#pragma unroll
+  for (int cc = 0; cc < CPT; cc += 2) w4[cc / 2] = pack_bf16x2(o[cc], o[cc + 1]);
+  if (CPT == 8) {
+    *reinterpret_cast<u32x4*>(op) = w4;
+  } else {
+    *reinterpret_cast<u32x2*>(op) = u32x2{w4[0], w4[1]};
+  }
+}
+
 template <int D, bool FP8>
 __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   using S = Shape<D, FP8>;
@@ -85,6 +103,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
   __shared__ __align__(16) unsigned char smem[SMEM];
   __shared__ int32_t s_pages[kSmallMaxPages];
+  __shared__ int32_t s_last;   // this workgroup finished its unit's last part
 
   const Item it = a.items[blockIdx.x];
   if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
@@ -360,15 +379,15 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   constexpr int CPT = D / 16;   // columns per thread
   const int row = threadIdx.x >> 4;
   const int c0 = (threadIdx.x & 15) * CPT;
-  if (row >= it.nrows) return;
+  const bool active = row < it.nrows;
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + row]);
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, cm[w * 16 + (active ? row : 0)]);
   float o[CPT];
 #pragma unroll
   for (int cc = 0; cc < CPT; ++cc) o[cc] = 0.f;
   float lse2 = -INFINITY;
-  if (M != -INFINITY) {
+  if (active && M != -INFINITY) {
     float den = 0.f;
     float wt[kWaves];
 #pragma unroll
@@ -385,29 +404,82 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
     for (int cc = 0; cc < CPT; ++cc) o[cc] *= inv;
     lse2 = M + log2f(den);
   }
-  const int rrho = it.row0 + row;
-  const int rj = rrho / G;
-  const int rhead = it.hk * G + (rrho - rj * G);
-  const int64_t rtok = (int64_t)rq.q_off + rj;
-  if (it.pbase < 0) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + rtok * a.o_st + (int64_t)rhead * a.o_sh + c0;
-    u32x4 w4;
-#pragma unroll
-    for (int cc = 0; cc < CPT; cc += 2) w4[cc / 2] = pack_bf16x2(o[cc], o[cc + 1]);
-    if (CPT == 8) {
-      *reinterpret_cast<u32x4*>(op) = w4;
-    } else {
-      *reinterpret_cast<u32x2*>(op) = u32x2{w4[0], w4[1]};
-    }
+  if (it.pbase < 0) {   // an unsplit unit: the final output
+    if (!active) return;
+    const int rrho = it.row0 + row;
+    const int rj = rrho / G;
+    const int rhead = it.hk * G + (rrho - rj * G);
+    const int64_t rtok = (int64_t)rq.q_off + rj;
+    store_row_bf16<CPT>(static_cast<uint16_t*>(a.out) + rtok * a.o_st + (int64_t)rhead * a.o_sh + c0, o);
     if (a.lse && (threadIdx.x & 15) == 0) a.lse[rtok * a.l_st + (int64_t)rhead * a.l_sh] = lse2 * kLn2;
-  } else {
+    return;
+  }
+  // ---- a split unit's parts are merged by whichever workgroup finishes last.
+  // Each part publishes its partial rows with device-coherent stores (scope
+  // "agent": they bypass the non-coherent per-XCD L2 instead of needing a whole
+  // L2 write-back), waits until they are complete, then counts itself in; the
+  // one that completes the count reads every part with device-coherent loads
+  // and merges them in part order, so the result does not depend on which
+  // workgroup that is.  Nothing waits on another workgroup.  The counter is
+  // reset for the next run.
+  if (it.merge0 < 0) {   // split, but merged by the merge kernel
+    if (!active) return;
     const int64_t prow = (int64_t)it.pbase + row;
     float* pp = a.part_o + prow * D + c0;
 #pragma unroll
     for (int cc = 0; cc < CPT; cc += 4)
       *reinterpret_cast<f32x4*>(pp + cc) = f32x4{o[cc], o[cc + 1], o[cc + 2], o[cc + 3]};
     if ((threadIdx.x & 15) == 0) a.part_lse[prow] = lse2;
+    return;
   }
+  if (active) {
+    const int64_t prow = (int64_t)it.pbase + row;
+    float* pp = a.part_o + prow * D + c0;
+#pragma unroll
+    for (int cc = 0; cc < CPT; ++cc)
+      __hip_atomic_store(pp + cc, o[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if ((threadIdx.x & 15) == 0)
+      __hip_atomic_store(a.part_lse + prow, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __builtin_amdgcn_s_waitcnt(kVmcntZero);   // this thread's partial stores are complete
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int parts = a.merges[it.merge0].count;
+    s_last = __hip_atomic_fetch_add(a.counters + it.merge0, 1, __ATOMIC_RELAXED,
+                                    __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  if (threadIdx.x == 0)
+    __hip_atomic_store(a.counters + it.merge0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (!active) return;
+  const MergeJob jb = a.merges[it.merge0 + row];
+  float m = -INFINITY;
+  for (int s = 0; s < jb.count; ++s)
+    m = fmaxf(m, __hip_atomic_load(a.part_lse + jb.pfirst + (int64_t)s * jb.pstride, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+  for (int cc = 0; cc < CPT; ++cc) o[cc] = 0.f;
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int s = 0; s < jb.count; ++s) {
+      const int64_t prow = jb.pfirst + (int64_t)s * jb.pstride;
+      const float w = exp2f(__hip_atomic_load(a.part_lse + prow, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) - m);   // -inf parts weigh 0
+      const float* po = a.part_o + prow * D + c0;
+#pragma unroll
+      for (int cc = 0; cc < CPT; ++cc)
+        o[cc] += w * __hip_atomic_load(po + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wsum += w;
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int cc = 0; cc < CPT; ++cc) o[cc] *= inv;
+  store_row_bf16<CPT>(static_cast<uint16_t*>(a.out) + (int64_t)jb.token * a.o_st + (int64_t)jb.head * a.o_sh + c0, o);
+  if (a.lse && (threadIdx.x & 15) == 0)
+    a.lse[(int64_t)jb.token * a.l_st + (int64_t)jb.head * a.l_sh] =
+        wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
 }
 
 }  // namespace

@@ -121,6 +121,8 @@ struct AttnArgs {
   float* lse;          // may be null
   float* part_o;       // [partial_rows, D]
   float* part_lse;     // [partial_rows], log2 domain
+  const MergeJob* merges;  // split small units' merge jobs (Item::merge0 indexes them)
+  int32_t* counters;   // arrival counter per split small unit, at Item::merge0
   int64_t q_st, q_sh;  // q strides (elements): token, head
   int64_t o_st, o_sh;
   int64_t l_st, l_sh;

@@ -22,7 +22,7 @@ constexpr int kSegCost = 3;       // start-up cost of a large-tile segment, in t
 constexpr int kMinPartTiles = 8;  // smallest KV part a large tile job is split into, in tiles
 constexpr double kTileBytes = 4.0e6;  // bytes the whole GPU streams in one large-tile time
 
-struct Item {          // one workgroup's work; 32 bytes
+struct Item {          // one workgroup's work; 48 bytes
   int32_t r;           // request
   int32_t hk;          // KV head
   int32_t row0;        // first unit row
@@ -31,6 +31,9 @@ struct Item {          // one workgroup's work; 32 bytes
   int32_t kv_end;      // one past the last KV position
   int32_t pbase;       // partial row of unit row row0 (-1: write out/lse directly)
   int32_t kind;        // 0 small tile, 1 large tile
+  int32_t merge0;      // split small tile: its unit's first merge job (also the
+                       // index of the unit's arrival counter); -1 otherwise
+  int32_t pad[3];
 };
 
 struct Req {           // per request; 16 bytes
@@ -52,8 +55,10 @@ struct MergeJob {      // one (query token, query head) finished from split part
 struct FixedCaps {     // capacities of a fixed plan
   int32_t batch = 0;   // requests
   int64_t tokens = 0;  // query tokens (the row count of q and out)
+  int64_t qlen = 0;    // query tokens of one request
   int64_t pages = 0;   // entries of the kv_indices buffer
-  int64_t small = 0, large = 0, merges = 0, partial_rows = 0;
+  int64_t small = 0, large = 0, partial_rows = 0;
+  int64_t merges_small = 0, merges_large = 0;   // merge jobs of small units / large jobs
 };
 
 }  // namespace ak
@@ -68,14 +73,16 @@ struct ak_plan_t {
   std::vector<int32_t> kv_lens;
   std::vector<ak::Req> reqs;
   std::vector<ak::Item> small_items, large_items;
-  std::vector<ak::MergeJob> merges;
+  std::vector<ak::MergeJob> merges;   // split small units' jobs first, then large jobs'
+  int64_t small_merges = 0;           // jobs of split small units
+  bool merge_in_kernel = false;       // small units merged inside the small-tile kernel
   int64_t partial_rows = 0;
   int64_t split_units = 0;
   // fixed plan: capacities the workspace is sized for (kernels are launched over
   // the whole capacity; entries past the live ones are padding with zero rows)
   bool fixed = false;
   ak::FixedCaps caps;
-  int64_t hw_small = 0, hw_large = 0, hw_merges = 0;   // entries uploaded so far
+  int64_t hw_small = 0, hw_large = 0, hw_msmall = 0, hw_mlarge = 0;   // entries uploaded so far
   const int32_t* kv_indices = nullptr;   // device, borrowed
   int64_t num_kv_pages = 0;
   // device workspace (one allocation)
@@ -85,6 +92,8 @@ struct ak_plan_t {
   ak::Item* d_small = nullptr;
   ak::Item* d_large = nullptr;
   ak::MergeJob* d_merges = nullptr;
+  ak::MergeJob* d_merges_large = nullptr;   // large jobs' merge list
+  int32_t* d_counters = nullptr;            // arrival counters of split small units
   float* d_part_o = nullptr;
   float* d_part_lse = nullptr;
   int device = 0;
@@ -102,10 +111,11 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
                           int32_t window, const ak_plan_opts* opts, int32_t num_cus, ak_plan_t* p);
 
 // Upper bounds on what build_plan_host emits for any batch of at most
-// caps->batch requests and caps->tokens query tokens (fills small, large,
-// merges, partial_rows).  Guaranteed for page sizes >= 8 and KV lengths up to
+// caps->batch requests, caps->tokens query tokens (caps->qlen in one request)
+// and caps->pages pages of B tokens (fills small, large, merges_small,
+// merges_large, partial_rows).  Guaranteed for page sizes >= 8 and KV lengths up to
 // max_splits * (1022 * page_size - 128) with Hkv * sum(L) <= 8 * num_cus * 4096.
-void fixed_capacities(int32_t Hkv, int32_t G, int32_t num_cus, const ak_plan_opts* opts,
+void fixed_capacities(int32_t Hkv, int32_t G, int32_t B, int32_t num_cus, const ak_plan_opts* opts,
                       FixedCaps* caps);
 
 }  // namespace ak

@@ -70,6 +70,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const int64_t max_splits = (opts && opts->max_splits > 0) ? opts->max_splits : 64;
   const int64_t min_chunk =
       (opts && opts->min_chunk > 0) ? round_up(opts->min_chunk, kKvAlign) : 256;
+  p->merge_in_kernel = opts && (opts->flags & AK_PLAN_MERGE_IN_KERNEL);
 
   // ---- lengths and validation
   p->kv_lens.assign(R, 0);
@@ -140,7 +141,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
           const int64_t nr = std::min<int64_t>(kLargeRows, rows - row0);
           int32_t lo, hi;
           kv_range(q, row0, row0 + nr, lo, hi);
-          jobs.push_back(Item{r, hk, (int32_t)row0, (int32_t)nr, lo, hi, -1, 1});
+          jobs.push_back(Item{r, hk, (int32_t)row0, (int32_t)nr, lo, hi, -1, 1, -1, {}});
         }
     }
   }
@@ -180,14 +181,17 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       S = std::max<int64_t>(S + 1, ceil_div(S * span, kSmallMaxPages - 1));
     }
     if (nparts <= 1) {
-      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0});
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0, -1, {}});
       continue;
     }
     const int64_t ubase = prow;
+    // the unit's first merge job, which a part merging in-kernel starts from
+    const int32_t m0 = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
     for (int64_t s = 0; s < nparts; ++s) {
       const int32_t a = (int32_t)std::max<int64_t>(u.lo, base + s * per);
       const int32_t b = (int32_t)std::min<int64_t>(u.hi, base + (s + 1) * per);
-      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0});
+      p->small_items.push_back(
+          Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0, m0, {}});
     }
     const Req& q = p->reqs[u.r];
     for (int32_t rho = 0; rho < u.rows; ++rho) {
@@ -203,6 +207,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     ++split_units;
     if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
   }
+  p->small_merges = (int64_t)p->merges.size();
   // ---- large tiles: one workgroup per segment, launched longest first so the
   // dispatcher's earliest-free-CU order approximates longest-processing-time
   // scheduling.  The cost of a segment is its 32-token KV tiles plus a fixed
@@ -311,35 +316,45 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
 // Bounds behind a fixed plan's workspace, following the planner above:
 //  * small units (<= kSmallRows rows) number at most Hkv * min(batch, tokens); a
-//    unit of len KV tokens gets at most ceil(len / chunk) parts and the chunk is
-//    at least 1/(8 num_cus) of all small-unit KV, so all parts together number at
-//    most units + 8 num_cus (inside the guaranteed range the 4096-token chunk cap
-//    and the page-table span never bind);
+//    unit of len KV tokens gets at most ceil(len / chunk) parts, and the chunk is
+//    at least min_chunk and at least 1/(8 num_cus) of all small-unit KV (which is
+//    at most Hkv * pages * B), so all parts together number at most units +
+//    min(8 num_cus, Hkv pages B / min_chunk) (inside the guaranteed range the
+//    4096-token chunk cap and the page-table span never bind);
 //  * large jobs number at most Hkv * (ceil(tokens G / kLargeRows) + requests with
 //    more than kSmallRows rows); splitting adds at most sum(t) / (share - kSegCost)
 //    segments, and share >= max(sum cost / num_cus, 2 kMinPartTiles + kSegCost)
 //    bounds that by 19/16 num_cus, which also bounds the split jobs;
 //  * partial rows and merge jobs follow from the rows of split units and jobs.
-void fixed_capacities(int32_t Hkv, int32_t G, int32_t num_cus, const ak_plan_opts* opts,
+void fixed_capacities(int32_t Hkv, int32_t G, int32_t B, int32_t num_cus, const ak_plan_opts* opts,
                       FixedCaps* c) {
   const int64_t S = (opts && opts->max_splits > 0) ? opts->max_splits : 64;
+  const int64_t min_chunk =
+      (opts && opts->min_chunk > 0) ? round_up(opts->min_chunk, kKvAlign) : 256;
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const int64_t R = c->batch, T = c->tokens;
   const int64_t rows_all = T * G * Hkv;               // unit rows over every KV head
   const int64_t units = (int64_t)Hkv * std::min<int64_t>(R, T);
-  c->small = std::min<int64_t>(units * S, units + 8 * cus);
+  const int64_t kv_small = std::min<int64_t>(c->pages, INT64_MAX / (64 * 256)) * B * Hkv;
+  c->small = std::min<int64_t>(units * S, units + std::min<int64_t>(8 * cus, ceil_div(kv_small, min_chunk)));
   int64_t part_small = std::min<int64_t>((int64_t)kSmallRows * c->small, S * rows_all);
   int64_t merge_small = std::min<int64_t>((int64_t)kSmallRows * units, rows_all);
   if (c->small == 0) part_small = merge_small = 0;
   // requests with more than kSmallRows rows have at least kSmallRows / G + 1 tokens
-  const int64_t r_large = std::min<int64_t>(R, T / (kSmallRows / G + 1));
-  const int64_t jobs = r_large == 0 ? 0 : Hkv * (ceil_div(T * G, kLargeRows) + r_large);
+  // (none when no request may have that many)
+  const int64_t Q = std::min<int64_t>(c->qlen > 0 ? c->qlen : T, T);
+  const int64_t r_large = Q * G <= kSmallRows ? 0 : std::min<int64_t>(R, T / (kSmallRows / G + 1));
+  const int64_t jobs =
+      r_large == 0 ? 0
+                   : Hkv * std::min<int64_t>(ceil_div(T * G, kLargeRows) + r_large,
+                                             r_large * ceil_div(Q * G, kLargeRows));
   const int64_t extra = ceil_div(19 * cus, 16);
   c->large = jobs == 0 ? 0 : jobs + extra;
   const int64_t part_large = jobs == 0 ? 0 : std::min<int64_t>(2 * (int64_t)kLargeRows * extra, S * rows_all);
   const int64_t merge_large = jobs == 0 ? 0 : std::min<int64_t>((int64_t)kLargeRows * extra, rows_all);
   c->partial_rows = part_small + part_large;
-  c->merges = merge_small + merge_large;
+  c->merges_small = merge_small;
+  c->merges_large = merge_large;
 }
 
 }  // namespace ak

@@ -49,7 +49,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 enum { kKinds = 5 };
 struct Profiler {
   std::mutex mu;
-  bool on = false;
+  int32_t mask = 0;   // kernel kinds timed (bit k = kind k)
   struct Rec {
     int kind;
     hipEvent_t a, b;
@@ -77,7 +77,7 @@ struct ProfScope {
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
   ProfScope(int k, hipStream_t st) : kind(k), s(st) {
-    if (!g_prof.on) return;
+    if (!(g_prof.mask & (1 << k))) return;
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
     if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return;
     std::lock_guard<std::mutex> lk(g_prof.mu);
@@ -264,6 +264,9 @@ ak_status acquire_ws(int device, size_t dev_bytes, size_t host_bytes, Workspace*
   bool found = false;
   {
     std::lock_guard<std::mutex> lk(g_pool_mu);
+    // the smallest idle workspace that fits (so plans of different sizes keep
+    // finding theirs, and no reallocation -- whose hipFree synchronises the
+    // device -- is needed in steady state); else the largest idle one, grown
     int idle_fit = -1, idle_any = -1, oldest = -1;
     for (size_t i = 0; i < g_pool.size(); ++i) {
       Workspace& c = g_pool[i];
@@ -271,10 +274,10 @@ ak_status acquire_ws(int device, size_t dev_bytes, size_t host_bytes, Workspace*
       if (oldest < 0) oldest = (int)i;
       if (c.done && hipEventQuery(c.done) != hipSuccess) continue;
       if (c.dev_bytes >= dev_bytes && c.host_bytes >= host_bytes) {
-        idle_fit = (int)i;
-        break;
+        if (idle_fit < 0 || c.dev_bytes < g_pool[idle_fit].dev_bytes) idle_fit = (int)i;
+      } else if (idle_any < 0 || c.dev_bytes > g_pool[idle_any].dev_bytes) {
+        idle_any = (int)i;
       }
-      if (idle_any < 0) idle_any = (int)i;
     }
     int pick = idle_fit >= 0 ? idle_fit : idle_any;
     if (pick < 0 && g_pool.size() >= kPoolMax) pick = oldest;
@@ -403,9 +406,12 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const size_t b_small = align256(p->small_items.size() * sizeof(Item));
     const size_t b_large = align256(p->large_items.size() * sizeof(Item));
     const size_t b_merge = align256(p->merges.size() * sizeof(MergeJob));
+    // arrival counters of split small units, uploaded as zeros (each run leaves
+    // them at zero again)
+    const size_t b_cnt = align256((size_t)p->small_merges * sizeof(int32_t));
     const size_t b_po = align256((size_t)p->partial_rows * p->D * sizeof(float));
     const size_t b_pl = align256((size_t)p->partial_rows * sizeof(float));
-    const size_t meta = b_req + b_small + b_large + b_merge;
+    const size_t meta = b_req + b_small + b_large + b_merge + b_cnt;
     p->d_bytes = meta + b_po + b_pl;
     if (p->d_bytes > 0) {
       st = acquire_ws(dev, p->d_bytes, meta, &p->ws);
@@ -419,6 +425,8 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       p->d_small = reinterpret_cast<Item*>(base + b_req);
       p->d_large = reinterpret_cast<Item*>(base + b_req + b_small);
       p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
+      p->d_merges_large = p->d_merges + p->small_merges;
+      p->d_counters = reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge);
       p->d_part_o = reinterpret_cast<float*>(base + meta);
       p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
       unsigned char* h = static_cast<unsigned char*>(p->ws.host);
@@ -430,6 +438,7 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       if (!p->merges.empty())
         std::memcpy(h + b_req + b_small + b_large, p->merges.data(),
                     p->merges.size() * sizeof(MergeJob));
+      if (b_cnt) std::memset(h + b_req + b_small + b_large + b_merge, 0, b_cnt);
       hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
       hipError_t e = hipSuccess;
       if (meta > 0) e = hipMemcpyAsync(p->d_buf, h, meta, hipMemcpyHostToDevice, s);
@@ -465,7 +474,7 @@ namespace ak {
 namespace {
 
 struct FixedLayout {
-  size_t req, small, large, merge, meta, po, pl, total;
+  size_t req, small, large, merge, merge_large, cnt, meta, po, pl, total;
 };
 
 FixedLayout fixed_layout(const FixedCaps& c, int D) {
@@ -474,7 +483,10 @@ FixedLayout fixed_layout(const FixedCaps& c, int D) {
   l.small = l.req + align256((size_t)c.batch * sizeof(Req));
   l.large = l.small + align256((size_t)c.small * sizeof(Item));
   l.merge = l.large + align256((size_t)c.large * sizeof(Item));
-  l.meta = l.merge + align256((size_t)c.merges * sizeof(MergeJob));
+  // the two merge lists are adjacent (one launch covers both on the fp32 path)
+  l.merge_large = l.merge + (size_t)c.merges_small * sizeof(MergeJob);
+  l.cnt = l.merge + align256((size_t)(c.merges_small + c.merges_large) * sizeof(MergeJob));
+  l.meta = l.cnt + align256((size_t)c.merges_small * sizeof(int32_t));
   l.po = l.meta;
   l.pl = l.po + align256((size_t)c.partial_rows * D * sizeof(float));
   l.total = l.pl + align256((size_t)c.partial_rows * sizeof(float));
@@ -484,14 +496,14 @@ FixedLayout fixed_layout(const FixedCaps& c, int D) {
 }  // namespace
 }  // namespace ak
 
-extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_pages,
-                                   const int32_t* kv_indices, int32_t num_qo_heads,
+extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_t max_query_len,
+                                   int64_t max_pages, const int32_t* kv_indices, int32_t num_qo_heads,
                                    int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                                    int32_t causal, int32_t window, const ak_plan_opts* opts,
                                    ak_plan_t** plan) {
   if (!plan) return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: null output pointer");
   *plan = nullptr;
-  if (max_batch < 0 || max_tokens < 0 || max_pages < 0)
+  if (max_batch < 0 || max_tokens < 0 || max_pages < 0 || max_query_len < 0)
     return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: negative capacity");
   if (max_tokens > INT32_MAX / 64 || max_pages > INT32_MAX)
     return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: capacity too large");
@@ -529,9 +541,11 @@ extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_
   p->fixed_opts.num_cus = cus;
   p->caps.batch = max_batch;
   p->caps.tokens = max_tokens;
+  p->caps.qlen = max_query_len > 0 ? std::min<int64_t>(max_query_len, max_tokens) : max_tokens;
   p->caps.pages = max_pages;
-  fixed_capacities(p->Hkv, p->G, cus, &p->fixed_opts, &p->caps);
-  if (p->caps.partial_rows > INT32_MAX / 2 || p->caps.merges > INT32_MAX / 2) {
+  fixed_capacities(p->Hkv, p->G, p->B, cus, &p->fixed_opts, &p->caps);
+  if (p->caps.partial_rows > INT32_MAX / 2 ||
+      p->caps.merges_small + p->caps.merges_large > INT32_MAX / 2) {
     recycle_plan(p);
     return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: split workspace too large");
   }
@@ -544,7 +558,8 @@ extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_
     if (l.total > 0) e = hipMalloc(&w.dev, l.total);
     if (e == hipSuccess && l.meta > 0) e = hipHostMalloc(&w.host, l.meta, hipHostMallocDefault);
     if (e == hipSuccess) e = hipEventCreateWithFlags(&w.done, hipEventDisableTiming);
-    // every item and merge job starts as padding (zero rows, zero parts)
+    // every item and merge job starts as padding (zero rows, zero parts), every
+    // arrival counter at zero
     if (e == hipSuccess && l.meta > 0) e = hipMemsetAsync(w.dev, 0, l.meta, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
@@ -562,6 +577,8 @@ extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_
     p->d_small = reinterpret_cast<Item*>(base + l.small);
     p->d_large = reinterpret_cast<Item*>(base + l.large);
     p->d_merges = reinterpret_cast<MergeJob*>(base + l.merge);
+    p->d_merges_large = reinterpret_cast<MergeJob*>(base + l.merge_large);
+    p->d_counters = reinterpret_cast<int32_t*>(base + l.cnt);
     p->d_part_o = reinterpret_cast<float*>(base + l.po);
     p->d_part_lse = reinterpret_cast<float*>(base + l.pl);
   }
@@ -589,6 +606,16 @@ extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
   } catch (const std::bad_alloc&) {
     st = fail(AK_ERR_OOM, "ak_plan_update: out of host memory");
   }
+  if (st == AK_OK) {
+    for (int32_t r = 0; r < t->R; ++r)
+      if (t->reqs[r].n > p->caps.qlen) {
+        std::ostringstream os;
+        os << "ak_plan_update: request " << r << " has " << t->reqs[r].n
+           << " query tokens, more than the plan's max_query_len " << p->caps.qlen;
+        st = fail(AK_ERR_SHAPE_MISMATCH, os.str());
+        break;
+      }
+  }
   if (st == AK_OK && (t->T > p->caps.tokens || t->num_kv_pages > p->caps.pages)) {
     std::ostringstream os;
     os << "ak_plan_update: " << t->T << " query tokens and " << t->num_kv_pages
@@ -597,7 +624,9 @@ extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
   }
   if (st == AK_OK && ((int64_t)t->small_items.size() > p->caps.small ||
                       (int64_t)t->large_items.size() > p->caps.large ||
-                      (int64_t)t->merges.size() > p->caps.merges || t->partial_rows > p->caps.partial_rows))
+                      t->small_merges > p->caps.merges_small ||
+                      (int64_t)t->merges.size() - t->small_merges > p->caps.merges_large ||
+                      t->partial_rows > p->caps.partial_rows))
     st = fail(AK_ERR_UNSUPPORTED, "ak_plan_update: the batch's work list exceeds the fixed workspace "
                                   "(KV lengths outside the guaranteed range)");
   if (st != AK_OK) {
@@ -622,7 +651,9 @@ extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
     stage(l.req, t->reqs.data(), (int64_t)t->reqs.size(), 0, sizeof(Req));
     stage(l.small, t->small_items.data(), (int64_t)t->small_items.size(), p->hw_small, sizeof(Item));
     stage(l.large, t->large_items.data(), (int64_t)t->large_items.size(), p->hw_large, sizeof(Item));
-    stage(l.merge, t->merges.data(), (int64_t)t->merges.size(), p->hw_merges, sizeof(MergeJob));
+    const int64_t ms = t->small_merges, ml = (int64_t)t->merges.size() - ms;
+    stage(l.merge, t->merges.data(), ms, p->hw_msmall, sizeof(MergeJob));
+    stage(l.merge_large, t->merges.data() + ms, ml, p->hw_mlarge, sizeof(MergeJob));
     if (e == hipSuccess) e = hipEventRecord(w.done, s);
     if (e != hipSuccess) {
       recycle_plan(t);
@@ -630,13 +661,15 @@ extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
     }
     p->hw_small = (int64_t)t->small_items.size();
     p->hw_large = (int64_t)t->large_items.size();
-    p->hw_merges = (int64_t)t->merges.size();
+    p->hw_msmall = ms;
+    p->hw_mlarge = ml;
   }
   p->R = t->R;
   p->T = t->T;
   p->num_kv_pages = t->num_kv_pages;
   p->partial_rows = t->partial_rows;
   p->split_units = t->split_units;
+  p->small_merges = t->small_merges;
   std::swap(p->kv_lens, t->kv_lens);
   std::swap(p->reqs, t->reqs);
   std::swap(p->small_items, t->small_items);
@@ -686,7 +719,12 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   // that a captured graph stays valid for every later update
   const int ns = p->fixed ? (int)p->caps.small : (int)p->small_items.size();
   const int nl = p->fixed ? (int)p->caps.large : (int)p->large_items.size();
-  const int nm = p->fixed ? (int)p->caps.merges : (int)p->merges.size();
+  // the merge kernel finishes split large jobs, and split small units too unless
+  // the plan merges those inside the small-tile kernel (bf16 / fp8 q only)
+  const int64_t n_ms = p->fixed ? p->caps.merges_small : p->small_merges;
+  const int64_t n_ml = p->fixed ? p->caps.merges_large : (int64_t)p->merges.size() - p->small_merges;
+  const bool all_merges = qd == AK_F32 || !p->merge_in_kernel;
+  const int nm = (int)(all_merges ? n_ms + n_ml : n_ml);
   if (T_run == 0 || (ns == 0 && nl == 0)) return AK_OK;
   if (!q->data || !out->data || !k_cache->data || !v_cache->data)
     return fail(AK_ERR_INVALID_ARG, "ak_run: null data pointer");
@@ -713,6 +751,8 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   a.out = out->data;
   a.lse = lse ? static_cast<float*>(lse->data) : nullptr;
   a.part_o = p->d_part_o;
+  a.merges = p->d_merges;
+  a.counters = p->d_counters;
   a.part_lse = p->d_part_lse;
   a.q_st = q->stride[0];
   a.q_sh = q->stride[1];
@@ -767,7 +807,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   }
   if (nm > 0) {
     MergeArgs m{};
-    m.jobs = p->d_merges;
+    m.jobs = all_merges ? p->d_merges : p->d_merges_large;
     m.part_o = p->d_part_o;
     m.part_lse = p->d_part_lse;
     m.out = out->data;
@@ -871,7 +911,7 @@ extern "C" ak_status ak_plan_info(const ak_plan_t* p, int64_t* info, int32_t n) 
                         p->partial_rows,
                         p->caps.small,
                         p->caps.large,
-                        p->caps.merges,
+                        p->caps.merges_small + p->caps.merges_large,
                         p->caps.partial_rows};
   for (int i = 0; i < n && i < 12; ++i) info[i] = v[i];
   return AK_OK;
@@ -888,7 +928,7 @@ extern "C" ak_status ak_plan_export(const ak_plan_t* p, int32_t* items, int64_t 
   int32_t* o = items;
   for (const auto* v : {&p->small_items, &p->large_items})
     for (const Item& it : *v) {
-      std::memcpy(o, &it, sizeof(Item));
+      std::memcpy(o, &it, 8 * sizeof(int32_t));   // the eight public fields
       o += 8;
     }
   return AK_OK;
@@ -965,9 +1005,10 @@ extern "C" ak_status ak_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t
   return AK_OK;
 }
 
-extern "C" ak_status ak_profile_enable(int32_t on) {
+extern "C" ak_status ak_profile_enable(int32_t kinds) {
+  if (kinds < 0) return fail(AK_ERR_INVALID_ARG, "ak_profile_enable: negative kind mask");
   std::lock_guard<std::mutex> lk(g_prof.mu);
-  g_prof.on = on != 0;
+  g_prof.mask = kinds;
   return AK_OK;
 }
 

@@ -170,6 +170,15 @@ def llama8b_decode(seed: int = 2, R: int = 64) -> Workload:
                      g_perm, 32, 8, 128, "bf16", "bf16", True, (-1,), spare_pages=64)
 
 
+def small_batch_decode(seed: int = 7, R: int = 8, lo: int = 256, hi: int = 1024) -> Workload:
+    """A few short decode requests (the launch-bound regime graph replay is for):
+    L ~ U{lo..hi}, otherwise shaped like llama8b_decode."""
+    g_len, g_perm, _, _ = _streams(seed)
+    kv_lens = g_len.integers(lo, hi, size=R, endpoint=True)
+    return _assemble("small_batch_decode_bf16", seed, np.ones(R, dtype=np.int64), kv_lens, 16,
+                     g_perm, 32, 8, 128, "bf16", "bf16", True, (-1,), spare_pages=16)
+
+
 def ragged_prefill(seed: int = 3, R: int = 8, n_range=(128, 2048), p_range=(0, 4096)) -> Workload:
     """8 extend requests, n ~ U{128..2048} new tokens over a cached prefix
     p ~ U{0..4096}, causal aligned to the sequence end, B = 1 (indices are token

@@ -23,7 +23,7 @@ def _csr(q_lens, kv_lens, B):
     return qo, kv, last
 
 
-def _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, lmax, kv_budget):
+def _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, lmax, kv_budget, page_budget=None):
     """Query and KV lengths of one batch of the given kind inside the maxima."""
     small_n = max(1, 16 // G)                      # most tokens a small unit can hold
     if kind == "decode":
@@ -57,6 +57,11 @@ def _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, lmax, kv_budget):
         L = np.maximum(n, np.full(R, cap))
     while Hkv * L.sum() > kv_budget:
         L = np.maximum(n, L // 2)
+    if page_budget is not None:
+        n, L = n[:page_budget], L[:page_budget]     # every request holds a page
+        while (-(-L // B)).sum() > page_budget and L.max() > 1:
+            L = np.maximum(np.minimum(n, 1), L // 2)
+            n = np.minimum(n, L)
     return n, L
 
 
@@ -72,21 +77,22 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("pages", [None, 3000, 200], ids=["pages_any", "pages_3000", "pages_200"])
 @pytest.mark.parametrize("case", CASES, ids=[f"c{i}" for i in range(len(CASES))])
-def test_fixed_capacity_holds_every_batch(case):
+def test_fixed_capacity_holds_every_batch(case, pages):
     max_batch, max_tokens, Hq, Hkv, B, cus, S = case
     G = Hq // Hkv
     splits = S or 64
     lmax = splits * (1022 * B - 128)
     kv_budget = 8 * cus * 4096
     plan = ak.ak_plan_fixed(max_batch, max_tokens, None, Hq, Hkv, 128, B, num_cus=cus,
-                            max_splits=S, host_only=True, max_pages=1 << 30)
+                            max_splits=S, host_only=True, max_pages=pages or (1 << 30))
     info = plan.info()
     rng = np.random.default_rng(max_batch + max_tokens + B)
     peak = dict.fromkeys(["small_items", "large_items", "merge_jobs", "partial_rows"], 0)
     for trial in range(60):
         kind = ["decode", "small_units", "many_jobs", "one_prefill", "mix"][trial % 5]
-        n, L = _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, lmax, kv_budget)
+        n, L = _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, lmax, kv_budget, pages)
         qo, kv, last = _csr(n, L, B)
         ak.ak_plan_update(plan, qo, kv, last)        # raises if the batch does not fit
         got = plan.info()
@@ -148,3 +154,36 @@ def test_fixed_plan_empty_batch_and_shrinking_batches():
         qo, kv, last = _csr([1] * R, [3000] * R, 16)
         ak.ak_plan_update(plan, qo, kv, last)
         assert plan.info()["batch_size"] == R
+
+
+@pytest.mark.parametrize("case", CASES[:4], ids=[f"c{i}" for i in range(4)])
+def test_fixed_capacity_with_query_length_bound(case):
+    max_batch, max_tokens, Hq, Hkv, B, cus, S = case
+    G = Hq // Hkv
+    for qlen in (1, 16 // G + 1, 300):
+        plan = ak.ak_plan_fixed(max_batch, max_tokens, None, Hq, Hkv, 128, B, num_cus=cus,
+                                max_splits=S, host_only=True, max_pages=1 << 30,
+                                max_query_len=qlen)
+        info = plan.info()
+        if qlen * G <= 16:
+            assert info["cap_large_items"] == 0          # pure decode: no large-tile launch
+        rng = np.random.default_rng(qlen)
+        for trial in range(40):
+            kind = ["decode", "small_units", "many_jobs", "one_prefill", "mix"][trial % 5]
+            n, L = _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, (S or 64) * 1000,
+                          8 * cus * 4096)
+            n = np.minimum(n, qlen)
+            L = np.maximum(L, n)
+            qo, kv, last = _csr(n, L, B)
+            ak.ak_plan_update(plan, qo, kv, last)
+            got = plan.info()
+            for k in ("small_items", "large_items", "merge_jobs", "partial_rows"):
+                cap = "cap_" + k
+                assert got[k] <= info[cap]
+    # a request longer than max_query_len is refused
+    plan = ak.ak_plan_fixed(8, 64, None, 32, 8, 128, 16, host_only=True, max_pages=100,
+                            max_query_len=1)
+    qo, kv, last = _csr([1, 2], [40, 40], 16)
+    with pytest.raises(ak.AkError) as e:
+        ak.ak_plan_update(plan, qo, kv, last)
+    assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH

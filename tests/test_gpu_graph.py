@@ -42,7 +42,8 @@ def _workload(seed, q_lens, kv_lens):
                     num_kv_heads=HKV, head_dim=D, name=f"graph_{seed}")
 
 
-def test_captured_step_replays_every_batch():
+@pytest.mark.parametrize("merge_in_kernel", [False, True], ids=["merge_launch", "merge_in_kernel"])
+def test_captured_step_replays_every_batch(merge_in_kernel):
     wls = [_workload(*b) for b in BATCHES]
     P = max(wl.num_pages for wl in wls)
     dev = "cuda"
@@ -61,7 +62,7 @@ def test_captured_step_replays_every_batch():
     v_new = torch.zeros_like(k_new)
     out = torch.zeros(T_MAX, HQ, D, dtype=torch.bfloat16, device=dev)
     lse = torch.zeros(T_MAX, HQ, dtype=torch.float32, device=dev)
-    plan = ak.ak_plan_fixed(R_MAX, T_MAX, kv_indices, HQ, HKV, D, B)
+    plan = ak.ak_plan_fixed(R_MAX, T_MAX, kv_indices, HQ, HKV, D, B, merge_in_kernel=merge_in_kernel)
     info = plan.info()
     say(f"[graph] capacities small={info['cap_small_items']} large={info['cap_large_items']} "
         f"merges={info['cap_merge_jobs']} partial_rows={info['cap_partial_rows']}")
@@ -118,7 +119,7 @@ def test_captured_step_replays_every_batch():
         assert torch.equal(out[:T], o1) and torch.equal(lse[:T], l1)
         # an eager ordinary plan over the same (stored) cache gives the same bits
         ref = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, d["kv_indices"], wl.last_page_len, HQ, HKV,
-                         D, B)
+                         D, B, merge_in_kernel=merge_in_kernel)
         eo = torch.empty(T, HQ, D, dtype=torch.bfloat16, device=dev)
         el = torch.empty(T, HQ, dtype=torch.float32, device=dev)
         ak.ak_run(ref, q[:T], k_cache, v_cache, out=eo, lse=el)
