@@ -259,7 +259,9 @@ void ak_plan_destroy(ak_plan_t* plan);
  *   q        [T, Hq, D]   F32 or BF16, T = qo_indptr[batch_size], D contiguous.
  *   k_cache,
  *   v_cache  [P, B, Hkv, D] same dtype as q, or FP8_E4M3 with BF16 q (the
- *            tensors' scale fields are the per-tensor dequantisation scales).
+ *            tensors' scale fields are the per-tensor dequantisation scales);
+ *            strides non-negative, rows 16-byte aligned, page and head strides
+ *            below 2 GiB and the slot stride times 256 below 2 GiB (in bytes).
  *   out      [T, Hq, D]   dtype of q (never FP8), D contiguous; written.
  *   lse      [T, Hq]      F32, or NULL; written.
  *
@@ -269,7 +271,7 @@ void ak_plan_destroy(ak_plan_t* plan);
  * Errors: AK_ERR_INVALID_ARG (null plan/tensor, host-only plan),
  * AK_ERR_SHAPE_MISMATCH (T, Hq, Hkv, D or B disagree with the plan -- a plan
  * built for fewer heads is rejected, never run), AK_ERR_UNSUPPORTED (dtype
- * combination, misaligned rows), AK_ERR_HIP.  An empty plan returns AK_OK and
+ * combination, misaligned rows, cache strides out of range), AK_ERR_HIP.  An empty plan returns AK_OK and
  * launches nothing.  With a fixed plan (ak_plan_fixed) T is the plan's
  * max_tokens, the launches cover its whole capacity whatever the live batch,
  * and rows past qo_indptr[batch_size] of the last update are left untouched. */

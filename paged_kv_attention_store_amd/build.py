@@ -24,6 +24,8 @@ HIP_FLAGS = [
     "-I", os.path.join(ROOT, "include"),
 ]
 CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+# per-source code generation options
+FILE_FLAGS = {}
 
 
 def _run(cmd):
@@ -45,7 +47,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for f in hip:
         obj = os.path.join(BUILD_DIR, f + ".o")
-        jobs.append([HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj])
+        jobs.append([HIPCC, *HIP_FLAGS, *FILE_FLAGS.get(f, []), "-c", os.path.join(CSRC, f), "-o", obj])
     for f in cpp:
         obj = os.path.join(BUILD_DIR, f + ".o")
         jobs.append(["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, f), "-o", obj])

@@ -449,16 +449,19 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) raw[i] = a.kv_indices[rq.page_off + (copy_token(b, i) >> a.log2B)];
   };
+  const uint32_t kps = (uint32_t)(a.k_sp * 2), kbs = (uint32_t)(a.k_sb * 2);
+  const uint32_t vps = (uint32_t)(a.v_sp * 2), vbs = (uint32_t)(a.v_sb * 2);
+  const int32_t pmax = (int32_t)min(a.num_pages - 1, (int64_t)INT32_MAX);
   auto issue_copy = [&](auto& kd, auto& vd, int b, const int32_t (&raw)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
       const int q = q0 + lane;
       const int t = q / CPR, j = q % CPR;
-      const int64_t page = raw[i] < 0 ? 0 : (raw[i] >= a.num_pages ? a.num_pages - 1 : (int64_t)raw[i]);
-      const int64_t slot = copy_token(b, i) & bmask;
-      const char* gk = kbase + (page * a.k_sp + slot * a.k_sb) * 2 + 16 * (j ^ kswz<D>(t));
-      const char* gv = vbase + (page * a.v_sp + slot * a.v_sb) * 2 + 16 * (j ^ vswz<D>(t));
+      const uint32_t page = (uint32_t)min(max(raw[i], 0), pmax);
+      const uint32_t slot = (uint32_t)(copy_token(b, i) & bmask);
+      const char* gk = kbase + ((uint64_t)page * kps + (slot * kbs + 16u * (j ^ kswz<D>(t))));
+      const char* gv = vbase + ((uint64_t)page * vps + (slot * vbs + 16u * (j ^ vswz<D>(t))));
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                        (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
                                        16, 0, 0);
@@ -670,6 +673,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     if (hf == 0) a.part_lse[prow] = lse2;
   }
 }
+
 
 }  // namespace
 

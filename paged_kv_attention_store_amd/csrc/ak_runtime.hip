@@ -736,8 +736,12 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
       (out->stride[0] * qb) % 16 || (out->stride[1] * qb) % 16)
     return fail(AK_ERR_UNSUPPORTED, "ak_run: q/out rows must be 16-byte aligned");
   for (const ak_tensor* c : {k_cache, v_cache})
-    for (int i = 0; i < 3; ++i)
+    for (int i = 0; i < 3; ++i) {
       if ((c->stride[i] * cb) % 16) return fail(AK_ERR_UNSUPPORTED, "ak_run: cache rows must be 16-byte aligned");
+      // page, slot and head offsets are formed in 32-bit byte units per page
+      if (c->stride[i] < 0 || c->stride[i] * cb >= (int64_t(1) << 31) / (i == 1 ? 256 : 1))
+        return fail(AK_ERR_UNSUPPORTED, "ak_run: cache strides must be non-negative and below 2 GiB");
+    }
   if (kd == AK_FP8_E4M3 && !(k_cache->scale > 0.f && v_cache->scale > 0.f &&
                              std::isfinite(k_cache->scale) && std::isfinite(v_cache->scale)))
     return fail(AK_ERR_INVALID_ARG, "ak_run: fp8 caches need positive finite scales");

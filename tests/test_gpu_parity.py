@@ -185,3 +185,13 @@ def test_run_rejects_mismatched_geometry():
     with pytest.raises(ak.AkError) as e:
         ak.ak_run(plan, d["q"], kc8, kc8)
     assert e.value.status == ak.AK_ERR_SHAPE_MISMATCH
+    # cache strides the kernels cannot address are refused before any launch
+    # (descriptors edited directly: no view of that size is ever built)
+    import ctypes
+    for dim, stride in ((0, 1 << 30), (1, 1 << 23)):
+        dq, dk, dv, do = (ak.tensor_desc(d["q"]), ak.tensor_desc(d["k_cache"]),
+                          ak.tensor_desc(d["v_cache"]), ak.tensor_desc(torch.empty_like(d["q"])))
+        dk.stride[dim] = stride
+        st = ak.lib().ak_run(plan.handle, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
+                             ctypes.byref(do), None, None)
+        assert st == ak.AK_ERR_UNSUPPORTED and "strides" in ak.ak_last_error()
