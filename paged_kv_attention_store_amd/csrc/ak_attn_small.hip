@@ -184,7 +184,10 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
     return (int64_t)s_pages[(t >> a.log2B) - first_page] * ps + (int64_t)(t & bmask) * bs;
   };
   // issue the HBM reads of local block k (rows past the item are clamped, so a
-  // prefetch past the last block reads valid memory)
+  // prefetch past the last block reads valid memory).  Every K/V byte is read
+  // once per run, so the loads are non-temporal: the streamed rows do not evict
+  // the page table, Q and partials from the caches (measured: 198 -> 181 us on
+  // the 64-request decode batch)
   auto issue = [&](Regs& rg, int k) {
     const int tb = kv_begin + (wave + kWaves * k) * BLK;
 #pragma unroll
@@ -193,14 +196,15 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < KL; ++p) {
         const int d0 = FP8 ? 64 * p + 16 * g4 : dmap<D>(p, g4);
-        rg.k[T][p] = *reinterpret_cast<const u32x4*>(row + d0 * EB);
+        rg.k[T][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + d0 * EB));
       }
     }
     const int cslot = lane % CPR;
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
       const int r = i * TPI + lane / CPR;
-      rg.v[i] = *reinterpret_cast<const u32x4*>(vbase + row_off(tb + r, vps, vbs) + cslot * 16);
+      rg.v[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4*>(vbase + row_off(tb + r, vps, vbs) + cslot * 16));
     }
   };
   // attention over local block k held in `rg`
