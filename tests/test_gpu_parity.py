@@ -195,3 +195,72 @@ def test_run_rejects_mismatched_geometry():
         st = ak.lib().ak_run(plan.handle, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                              ctypes.byref(do), None, None)
         assert st == ak.AK_ERR_UNSUPPORTED and "strides" in ak.ak_last_error()
+
+
+# ------------------------------------------------------ layouts and splits
+
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_strided_views(kd):
+    # K and V interleaved in one pool [P, B, 2, Hkv, D], q a slice of a fused
+    # [T, Hq + 2 Hkv, D] projection, out a slice of a wider buffer, lse strided
+    wl = W.custom(seed=17, q_lens=[1, 1, 90, 3], kv_lens=[700, 33, 300, 2100], page_size=16,
+                  num_qo_heads=16, num_kv_heads=4, head_dim=128, kv_dtype=kd, windows=(-1, 64),
+                  name=f"strided_{kd}")
+    say(f"[layout] strided views, {kd} caches")
+    d = prepare(wl)
+    P, B, H, D = d["k_cache"].shape
+    pool = torch.empty(P, B, 2, H, D, dtype=d["k_cache"].dtype, device="cuda")
+    pool[:, :, 0] = d["k_cache"]
+    pool[:, :, 1] = d["v_cache"]
+    kc, vc = pool[:, :, 0], pool[:, :, 1]
+    T, Hq = wl.total_q, wl.num_qo_heads
+    qkv = torch.empty(T, Hq + 2 * H, D, dtype=d["q"].dtype, device="cuda")
+    qkv[:, :Hq] = d["q"]
+    q = qkv[:, :Hq]
+    assert not q.is_contiguous() and not kc.is_contiguous()
+    for window in wl.windows:
+        for kw in ({}, {"min_chunk": 64, "num_cus": 1024}):
+            plan = plan_for(wl, d, window, **kw)
+            wide = torch.full((T, Hq + 4, D), float("nan"), dtype=d["q"].dtype, device="cuda")
+            out = wide[:, 2:2 + Hq]
+            lse_wide = torch.full((T, 2 * Hq), float("nan"), device="cuda")
+            lse = lse_wide[:, ::2]
+            ak.ak_run(plan, q, kc, vc, out=out, lse=lse, k_scale=wl.kv_scale, v_scale=wl.kv_scale)
+            torch.cuda.synchronize()
+            check(wl, out, lse, window)
+            # nothing outside the views was written
+            assert torch.all(torch.isnan(wide[:, :2].float())) and torch.all(torch.isnan(wide[:, 2 + Hq:].float()))
+            assert torch.all(torch.isnan(lse_wide[:, 1::2]))
+
+
+def test_page_table_span_forces_more_splits():
+    # page size 1 and at most 2 splits: a part may not span more than the 1024
+    # pages a small tile stages, so the planner cuts more parts than max_splits
+    wl = W.custom(seed=23, q_lens=[1, 1, 2], kv_lens=[5000, 3000, 2049], page_size=1,
+                  num_qo_heads=8, num_kv_heads=2, head_dim=128, name="span_split")
+    say("[splits] page-table span")
+    d = prepare(wl)
+    plan = plan_for(wl, d, -1, max_splits=2)
+    items, _ = ak.ak_plan_export(plan)
+    per_unit = {}
+    for it in items.tolist():
+        per_unit[(it[0], it[1])] = per_unit.get((it[0], it[1]), 0) + 1
+        assert it[5] - it[4] <= 1024          # each part within one staged page table
+    assert max(per_unit.values()) > 2
+    out, lse = run(wl, d, plan)
+    check(wl, out, lse, -1)
+
+
+def test_long_prefill_split_along_kv():
+    # one long extend over a long prefix: its few 256-row jobs would set the
+    # makespan, so the planner splits them along KV and merges the parts
+    wl = W.custom(seed=29, q_lens=[512], kv_lens=[16384], page_size=16, num_qo_heads=32,
+                  num_kv_heads=8, head_dim=128, name="long_prefill")
+    say("[splits] long prefill, large tiles split along KV")
+    d = prepare(wl)
+    plan = plan_for(wl, d, -1)
+    info = ak.ak_plan_info(plan)
+    say(f"  plan {info}")
+    assert info["large_items"] > 64 and info["merge_jobs"] > 0
+    out, lse = run(wl, d, plan)
+    check(wl, out, lse, -1, rows_of=lambda r: _sample_rows(wl, r, k=48))
