@@ -467,7 +467,7 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
-    ap.add_argument("--also", default="prefill",
+    ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph",
                     help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph "
                          "('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
