@@ -338,7 +338,8 @@ ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak
  * on `stream`, padding out entries the previous batch used past the new one's
  * end.  It must be issued on the stream that replays the runs, between replays,
  * and outside capture.  The plan's workspace holds one batch: an update takes
- * effect for every later replay.
+ * effect for every later replay.  Either call on a stream that is being
+ * captured returns AK_ERR_INVALID_ARG.
  *
  * ak_run with a fixed plan launches every kernel over the capacity (fixed
  * grids), so a run captured once replays correctly after any update.  Padding

@@ -477,6 +477,13 @@ struct FixedLayout {
   size_t req, small, large, merge, merge_large, cnt, meta, po, pl, total;
 };
 
+// plan creation and updates synchronise and copy from the host: never inside a
+// stream capture
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  return hipStreamIsCapturing(s, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone;
+}
+
 FixedLayout fixed_layout(const FixedCaps& c, int D) {
   FixedLayout l{};
   l.req = 0;
@@ -552,6 +559,10 @@ extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_
   if (!host_only) {
     const FixedLayout l = fixed_layout(p->caps, p->D);
     hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
+    if (capturing(s)) {
+      recycle_plan(p);
+      return fail(AK_ERR_INVALID_ARG, "ak_plan_fixed: the stream is being captured");
+    }
     Workspace& w = p->ws;
     w.device = dev;
     hipError_t e = hipSuccess;
@@ -632,6 +643,10 @@ extern "C" ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr,
   if (st != AK_OK) {
     recycle_plan(t);
     return st;
+  }
+  if (!p->host_only && capturing(static_cast<hipStream_t>(stream))) {
+    recycle_plan(t);
+    return fail(AK_ERR_INVALID_ARG, "ak_plan_update: the stream is being captured");
   }
   if (!p->host_only) {
     const FixedLayout l = fixed_layout(p->caps, p->D);

@@ -126,3 +126,22 @@ def test_captured_step_replays_every_batch(merge_in_kernel):
         torch.cuda.synchronize()
         assert torch.equal(eo, o1) and torch.equal(el, l1)
         check(wl, o1, l1, -1)
+
+
+def test_plan_calls_refused_inside_capture():
+    # creating or updating a fixed plan synchronises and copies from the host:
+    # inside a capture both are refused with a clear error (and nothing is recorded)
+    kv_indices = torch.zeros(64, dtype=torch.int32, device="cuda")
+    plan = ak.ak_plan_fixed(4, 8, kv_indices, HQ, HKV, D, B)
+    g = torch.cuda.CUDAGraph()
+    errors = []
+    with torch.cuda.graph(g):
+        for call in (lambda: ak.ak_plan_fixed(4, 8, kv_indices, HQ, HKV, D, B),
+                     lambda: ak.ak_plan_update(plan, [0, 1], [0, 1], [5])):
+            try:
+                call()
+            except ak.AkError as e:
+                errors.append((e.status, ak.ak_last_error()))
+    assert [s for s, _ in errors] == [ak.AK_ERR_INVALID_ARG] * 2
+    assert all("captured" in m for _, m in errors)
+    ak.ak_plan_update(plan, [0, 1], [0, 1], [5])      # outside the capture: fine
