@@ -347,7 +347,7 @@ ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_a, const ak
  *
  * The capacity always suffices for page_size >= 8, KV lengths up to
  * max_splits * (1022 * page_size - 128) and num_kv_heads * sum L_r up to
- * 8 * num_cus * 4096; beyond that ak_plan_update may return AK_ERR_UNSUPPORTED
+ * 6 * num_cus * 4096; beyond that ak_plan_update may return AK_ERR_UNSUPPORTED
  * and leaves the plan as it was.
  * Errors: AK_ERR_INVALID_ARG (null pointer, negative capacity, update of a
  * non-fixed plan), AK_ERR_UNSUPPORTED, AK_ERR_SHAPE_MISMATCH (batch larger than

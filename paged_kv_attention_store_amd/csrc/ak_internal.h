@@ -21,6 +21,7 @@ constexpr int kBlockTiles = 4;    // tiles per KV block of the large-tile kernel
 constexpr int kSegCost = 3;       // start-up cost of a large-tile segment, in tiles
 constexpr int kMinPartTiles = 8;  // smallest KV part a large tile job is split into, in tiles
 constexpr double kTileBytes = 4.0e6;  // bytes the whole GPU streams in one large-tile time
+constexpr int kPartsPerCu = 6;    // decode KV parts per compute unit the split aims at
 
 struct Item {          // one workgroup's work; 48 bytes
   int32_t r;           // request
@@ -114,7 +115,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
 // caps->batch requests, caps->tokens query tokens (caps->qlen in one request)
 // and caps->pages pages of B tokens (fills small, large, merges_small,
 // merges_large, partial_rows).  Guaranteed for page sizes >= 8 and KV lengths up to
-// max_splits * (1022 * page_size - 128) with Hkv * sum(L) <= 8 * num_cus * 4096.
+// max_splits * (1022 * page_size - 128) with Hkv * sum(L) <= kPartsPerCu * num_cus * 4096.
 void fixed_capacities(int32_t Hkv, int32_t G, int32_t B, int32_t num_cus, const ak_plan_opts* opts,
                       FixedCaps* caps);
 

@@ -146,9 +146,9 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     }
   }
 
-  // Split size: about eight KV chunks per compute unit over the whole batch,
+  // Split size: about kPartsPerCu KV chunks per compute unit over the whole batch,
   // between min_chunk and 4096 tokens, in multiples of kKvAlign.
-  int64_t chunk = ceil_div(std::max<int64_t>(small_tokens, 1), (int64_t)p->num_cus * 8);
+  int64_t chunk = ceil_div(std::max<int64_t>(small_tokens, 1), (int64_t)p->num_cus * kPartsPerCu);
   chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
   chunk = std::max<int64_t>(chunk, min_chunk);
 
@@ -317,9 +317,9 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
 // Bounds behind a fixed plan's workspace, following the planner above:
 //  * small units (<= kSmallRows rows) number at most Hkv * min(batch, tokens); a
 //    unit of len KV tokens gets at most ceil(len / chunk) parts, and the chunk is
-//    at least min_chunk and at least 1/(8 num_cus) of all small-unit KV (which is
+//    at least min_chunk and at least 1/(kPartsPerCu num_cus) of all small-unit KV (which is
 //    at most Hkv * pages * B), so all parts together number at most units +
-//    min(8 num_cus, Hkv pages B / min_chunk) (inside the guaranteed range the
+//    min(kPartsPerCu num_cus, Hkv pages B / min_chunk) (inside the guaranteed range the
 //    4096-token chunk cap and the page-table span never bind);
 //  * large jobs number at most Hkv * (ceil(tokens G / kLargeRows) + requests with
 //    more than kSmallRows rows); splitting adds at most sum(t) / (share - kSegCost)
@@ -336,7 +336,7 @@ void fixed_capacities(int32_t Hkv, int32_t G, int32_t B, int32_t num_cus, const 
   const int64_t rows_all = T * G * Hkv;               // unit rows over every KV head
   const int64_t units = (int64_t)Hkv * std::min<int64_t>(R, T);
   const int64_t kv_small = std::min<int64_t>(c->pages, INT64_MAX / (64 * 256)) * B * Hkv;
-  c->small = std::min<int64_t>(units * S, units + std::min<int64_t>(8 * cus, ceil_div(kv_small, min_chunk)));
+  c->small = std::min<int64_t>(units * S, units + std::min<int64_t>((int64_t)kPartsPerCu * cus, ceil_div(kv_small, min_chunk)));
   int64_t part_small = std::min<int64_t>((int64_t)kSmallRows * c->small, S * rows_all);
   int64_t merge_small = std::min<int64_t>((int64_t)kSmallRows * units, rows_all);
   if (c->small == 0) part_small = merge_small = 0;

@@ -84,7 +84,7 @@ def test_fixed_capacity_holds_every_batch(case, pages):
     G = Hq // Hkv
     splits = S or 64
     lmax = splits * (1022 * B - 128)
-    kv_budget = 8 * cus * 4096
+    kv_budget = 6 * cus * 4096
     plan = ak.ak_plan_fixed(max_batch, max_tokens, None, Hq, Hkv, 128, B, num_cus=cus,
                             max_splits=S, host_only=True, max_pages=pages or (1 << 30))
     info = plan.info()
@@ -171,7 +171,7 @@ def test_fixed_capacity_with_query_length_bound(case):
         for trial in range(40):
             kind = ["decode", "small_units", "many_jobs", "one_prefill", "mix"][trial % 5]
             n, L = _batch(rng, kind, max_batch, max_tokens, G, Hkv, B, (S or 64) * 1000,
-                          8 * cus * 4096)
+                          6 * cus * 4096)
             n = np.minimum(n, qlen)
             L = np.maximum(L, n)
             qo, kv, last = _csr(n, L, B)
