@@ -19,7 +19,8 @@ Further workloads (--also) are reported under their names: the ragged extend
 batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
 the mixed chunked-prefill + decode step with full and sliding-window layers
 ("mixed"), the fp8 long-context decode ("longfp8"), decode requests sharing
-a 4096-token prefix run plainly and as a cascade ("cascade"), and a small
+a 4096-token prefix run plainly (with the shared-pages flag, and streamed) and
+as a cascade ("cascade"), and a small
 decode batch issued eagerly and as a replayed graph over a fixed plan ("graph").
 
 The CPU baseline times the float64 oracle on a sample of the decode batch.
@@ -331,7 +332,11 @@ def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
     T, hq, hkv, D, B = wl.total_q, wl.num_qo_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
     k = wl.extra["shared_pages"]
     idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
-    plain = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B)
+    # plain decode twice: K/V streamed (the default) and with the shared-pages
+    # flag (cached reads, so the shared prefix is served from the caches)
+    plain_stream = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B)
+    plain = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B,
+                       shared_pages=True)
     idx_s = torch.from_numpy(wl.kv_indices[:k].astype(np.int32)).to(dev)
     shared = ak.ak_plan([0, T], [0, k], idx_s, [B], hq, hkv, D, B, causal=False)
     sx = np.concatenate([wl.kv_indices[wl.kv_indptr[r] + k:wl.kv_indptr[r + 1]]
@@ -346,6 +351,10 @@ def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
     def plain_pass():
         for L in layers:
             ak.ak_run(plain, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+
+    def plain_stream_pass():
+        for L in layers:
+            ak.ak_run(plain_stream, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
 
     def cascade_pass():
         for L in layers:
@@ -365,17 +374,20 @@ def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / (steps * n_layers)
 
-    plain_us, cascade_us = timed(plain_pass), timed(cascade_pass)
+    plain_us, stream_us, cascade_us = timed(plain_pass), timed(plain_stream_pass), timed(cascade_pass)
     per_tok = hkv * D * 2 * EB[wl.kv_dtype]
     plain_bytes = decode_bytes(wl)
     cascade_bytes = plain_bytes - (wl.batch_size - 1) * k * B * per_tok
     res = {"workload": wl.name, "layers": n_layers, "shared_tokens": k * B,
-           "plain_us_per_layer": round(plain_us, 1), "cascade_us_per_layer": round(cascade_us, 1),
+           "plain_us_per_layer": round(plain_us, 1),
+           "plain_streaming_us_per_layer": round(stream_us, 1),
+           "cascade_us_per_layer": round(cascade_us, 1),
            "speedup": round(plain_us / cascade_us, 2),
            "plain_GBs": round(plain_bytes / (plain_us * 1e-6) / 1e9, 1),
            "cascade_GBs": round(cascade_bytes / (cascade_us * 1e-6) / 1e9, 1),
            "plain_bytes": plain_bytes, "cascade_bytes": cascade_bytes}
-    log(f"[bench] {wl.name}: plain {plain_us:.1f} us/layer ({res['plain_GBs']} GB/s), cascade "
+    log(f"[bench] {wl.name}: plain {plain_us:.1f} us/layer ({res['plain_GBs']} GB/s; "
+        f"{stream_us:.1f} with streamed K/V), cascade "
         f"{cascade_us:.1f} us/layer ({res['cascade_GBs']} GB/s of its own bytes), "
         f"x{res['speedup']}")
     del layers

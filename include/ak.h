@@ -175,10 +175,14 @@ typedef struct ak_plan_t ak_plan_t;    /* opaque; owned by the library */
 
 enum {
   AK_PLAN_HOST_ONLY = 1,        /* build the work list without touching the GPU           */
-  AK_PLAN_MERGE_IN_KERNEL = 2   /* split decode units (<= 16 rows) are merged by the last of
+  AK_PLAN_MERGE_IN_KERNEL = 2,  /* split decode units (<= 16 rows) are merged by the last of
                                    their parts inside the attention kernel (bf16 q) instead
                                    of by a separate merge launch: one launch fewer per run,
                                    for launch-bound small batches; slower for large ones  */
+  AK_PLAN_SHARED_PAGES = 4      /* requests of the batch share pages (a common prefix): decode
+                                   reads K/V with ordinary cached loads so later readers of a
+                                   shared page hit the caches; by default they are streamed
+                                   (read once, kept out of the caches)                    */
 };
 
 typedef struct {
@@ -189,7 +193,8 @@ typedef struct {
                             only when a split would span more than 1024 pages (page
                             size 1 or 2 with long contexts)                        */
   int32_t min_chunk;     /* smallest KV split in tokens; 0 = library default       */
-  int32_t flags;         /* AK_PLAN_HOST_ONLY | AK_PLAN_MERGE_IN_KERNEL              */
+  int32_t flags;         /* AK_PLAN_HOST_ONLY | AK_PLAN_MERGE_IN_KERNEL |
+                            AK_PLAN_SHARED_PAGES                                     */
   void* stream;          /* stream for the plan's upload; NULL = default stream     */
 } ak_plan_opts;
 

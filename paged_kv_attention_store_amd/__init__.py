@@ -42,6 +42,7 @@ STATUS_NAMES = {0: "AK_OK", -1: "AK_ERR_INVALID_ARG", -2: "AK_ERR_UNSUPPORTED",
 AK_F32, AK_BF16, AK_FP8_E4M3, AK_I32, AK_I64 = 0, 1, 2, 3, 4
 AK_PLAN_HOST_ONLY = 1
 AK_PLAN_MERGE_IN_KERNEL = 2
+AK_PLAN_SHARED_PAGES = 4
 AK_PROFILE_ALL = 0x1F
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
@@ -222,7 +223,7 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
             head_dim: int, page_size: int, causal: bool = True, window: int = -1,
             sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
             min_chunk: int = 0, host_only: bool = False, merge_in_kernel: bool = False,
-            stream=None) -> Plan:
+            shared_pages: bool = False, stream=None) -> Plan:
     """Build a plan.  qo_indptr, kv_indptr and last_page_len are host arrays
     (anything NumPy accepts); kv_indices is a device int32 tensor (or None for a
     host-only plan)."""
@@ -237,8 +238,9 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
     opts.num_cus = int(num_cus)
     opts.max_splits = int(max_splits)
     opts.min_chunk = int(min_chunk)
-    opts.flags = (AK_PLAN_HOST_ONLY if host_only else 0) | (
-        AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0)
+    opts.flags = ((AK_PLAN_HOST_ONLY if host_only else 0) |
+                  (AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None:
@@ -260,7 +262,7 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
                   window: int = -1, sm_scale: float | None = None, num_cus: int = 0,
                   max_splits: int = 0, min_chunk: int = 0, host_only: bool = False,
                   max_pages: int | None = None, max_query_len: int = 0,
-                  merge_in_kernel: bool = False, stream=None) -> Plan:
+                  merge_in_kernel: bool = False, shared_pages: bool = False, stream=None) -> Plan:
     """A plan with a fixed device workspace for graph capture.  kv_indices is the
     stable device int32 buffer later batches write their page ids into (its size
     is the page capacity); host-only plans take None and max_pages.  max_query_len
@@ -270,8 +272,9 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
     opts.num_cus = int(num_cus)
     opts.max_splits = int(max_splits)
     opts.min_chunk = int(min_chunk)
-    opts.flags = (AK_PLAN_HOST_ONLY if host_only else 0) | (
-        AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0)
+    opts.flags = ((AK_PLAN_HOST_ONLY if host_only else 0) |
+                  (AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None and not host_only:

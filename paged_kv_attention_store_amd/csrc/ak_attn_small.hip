@@ -92,7 +92,15 @@ __device__ __forceinline__ void store_row_bf16(uint16_t* op, const float* o) {
   }
 }
 
-template <int D, bool FP8>
+// kv_load: one 16-byte K/V read, streaming (non-temporal) unless the batch's
+// requests share pages
+template <bool STREAM>
+__device__ __forceinline__ u32x4 kv_load(const void* p) {
+  if (STREAM) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+template <int D, bool FP8, bool STREAM>
 __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   using S = Shape<D, FP8>;
   constexpr int BLK = S::BLK, NT = S::NT, NSTEP = S::NSTEP, NDT = S::NDT, EB = S::EB;
@@ -184,10 +192,11 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
     return (int64_t)s_pages[(t >> a.log2B) - first_page] * ps + (int64_t)(t & bmask) * bs;
   };
   // issue the HBM reads of local block k (rows past the item are clamped, so a
-  // prefetch past the last block reads valid memory).  Every K/V byte is read
-  // once per run, so the loads are non-temporal: the streamed rows do not evict
+  // prefetch past the last block reads valid memory).  When every K/V byte is
+  // read once per run the loads are non-temporal: the streamed rows do not evict
   // the page table, Q and partials from the caches (measured: 198 -> 181 us on
-  // the 64-request decode batch)
+  // the 64-request decode batch).  When requests share pages (a common prefix)
+  // ordinary loads let the later readers of a page hit the caches.
   auto issue = [&](Regs& rg, int k) {
     const int tb = kv_begin + (wave + kWaves * k) * BLK;
 #pragma unroll
@@ -196,15 +205,14 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
       for (int p = 0; p < KL; ++p) {
         const int d0 = FP8 ? 64 * p + 16 * g4 : dmap<D>(p, g4);
-        rg.k[T][p] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + d0 * EB));
+        rg.k[T][p] = kv_load<STREAM>(row + d0 * EB);
       }
     }
     const int cslot = lane % CPR;
 #pragma unroll
     for (int i = 0; i < VL; ++i) {
       const int r = i * TPI + lane / CPR;
-      rg.v[i] = __builtin_nontemporal_load(
-          reinterpret_cast<const u32x4*>(vbase + row_off(tb + r, vps, vbs) + cslot * 16));
+      rg.v[i] = kv_load<STREAM>(vbase + row_off(tb + r, vps, vbs) + cslot * 16);
     }
   };
   // attention over local block k held in `rg`
@@ -488,22 +496,25 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
+hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, bool shared_pages,
+                             hipStream_t s) {
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
-  if (D == 128 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_small_kernel<128, false>), grid, dim3(256), 0, s, a);
-  } else if (D == 64 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_small_kernel<64, false>), grid, dim3(256), 0, s, a);
-  } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_small_kernel<128, true>), grid, dim3(256), 0, s, a);
-  } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_small_kernel<64, true>), grid, dim3(256), 0, s, a);
-  } else {
-    return hipErrorInvalidValue;
+#define AK_SMALL_CASE(DD, F8)                                                                \
+  if (D == DD && kv_dtype == (F8 ? AK_FP8_E4M3 : AK_BF16)) {                                 \
+    if (shared_pages)                                                                        \
+      hipLaunchKernelGGL((attn_small_kernel<DD, F8, false>), grid, dim3(256), 0, s, a);      \
+    else                                                                                     \
+      hipLaunchKernelGGL((attn_small_kernel<DD, F8, true>), grid, dim3(256), 0, s, a);       \
+    return hipGetLastError();                                                                \
   }
-  return hipGetLastError();
+  AK_SMALL_CASE(128, false)
+  AK_SMALL_CASE(64, false)
+  AK_SMALL_CASE(128, true)
+  AK_SMALL_CASE(64, true)
+#undef AK_SMALL_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ak

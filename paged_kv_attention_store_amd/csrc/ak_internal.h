@@ -77,6 +77,7 @@ struct ak_plan_t {
   std::vector<ak::MergeJob> merges;   // split small units' jobs first, then large jobs'
   int64_t small_merges = 0;           // jobs of split small units
   bool merge_in_kernel = false;       // small units merged inside the small-tile kernel
+  bool shared_pages = false;          // requests share pages: cached (not streaming) K/V reads
   int64_t partial_rows = 0;
   int64_t split_units = 0;
   // fixed plan: capacities the workspace is sized for (kernels are launched over

@@ -71,6 +71,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   const int64_t min_chunk =
       (opts && opts->min_chunk > 0) ? round_up(opts->min_chunk, kKvAlign) : 256;
   p->merge_in_kernel = opts && (opts->flags & AK_PLAN_MERGE_IN_KERNEL);
+  p->shared_pages = opts && (opts->flags & AK_PLAN_SHARED_PAGES);
 
   // ---- lengths and validation
   p->kv_lens.assign(R, 0);

@@ -820,7 +820,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
     if (ns > 0) {
       a.items = p->d_small;
       ProfScope ps(1, s);
-      e = launch_attn_small(a, ns, p->D, kd, s);
+      e = launch_attn_small(a, ns, p->D, kd, p->shared_pages, s);
     }
     if (e != hipSuccess) return hip_fail(e, "ak_run: small-tile attention");
   }

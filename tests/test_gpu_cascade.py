@@ -154,6 +154,17 @@ def test_shared_prefix_cascade_equals_decode(case):
     out, lse = ak.ak_merge_states(o1, l1, o2, l2)
     torch.cuda.synchronize()
     check(wl, out, lse, -1)
+    # plain decode of the same batch with cached (shared-pages) and streamed K/V
+    # reads: the flag changes cache behaviour only, so the bits are the same
+    runs = []
+    for shared in (True, False):
+        pl = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, d["kv_indices"], wl.last_page_len, hq, hkv, D,
+                        B, shared_pages=shared)
+        runs.append(ak.ak_run(pl, d["q"], d["k_cache"], d["v_cache"],
+                              lse=torch.empty(T, hq, device="cuda")))
+    torch.cuda.synchronize()
+    assert torch.equal(runs[0][0], runs[1][0]) and torch.equal(runs[0][1], runs[1][1])
+    check(wl, runs[0][0], runs[0][1], -1)
 
 
 def test_noncausal_more_queries_than_keys():
