@@ -172,13 +172,31 @@ def tensor_desc(t, scale: float = 1.0) -> AkTensor:
     return d
 
 
+_DESC_CACHE: dict = {}
+_DESC_CACHE_MAX = 4096
+
+
+def _desc(t, scale: float = 1.0) -> AkTensor:
+    """tensor_desc for the entry points: a descriptor is a pure function of the
+    tensor's address, dtype, shape, strides and scale, so one built earlier for
+    the same values is reused (serving loops pass the same tensors every step).
+    Shared objects: never modify what this returns."""
+    key = (t.data_ptr(), t.dtype, t.shape, t.stride(), scale)
+    d = _DESC_CACHE.get(key)
+    if d is None:
+        if len(_DESC_CACHE) >= _DESC_CACHE_MAX:
+            _DESC_CACHE.clear()
+        d = _DESC_CACHE[key] = tensor_desc(t, scale)
+    return d
+
+
 def _stream_ptr(stream):
     import torch
 
     if stream is None:
         if not torch.cuda.is_available():
             return ctypes.c_void_p(None)      # host-only paths never launch
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(torch.cuda.current_device()))
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -192,8 +210,8 @@ def _host_i32(a):
 def ak_store_kv(k, v, slot_mapping, k_cache, v_cache, k_scale: float = 1.0, v_scale: float = 1.0,
                 stream=None) -> None:
     """Scatter k/v [N, Hkv, D] into the caches [P, B, Hkv, D] at slot_mapping (int64)."""
-    dk, dv, ds = tensor_desc(k), tensor_desc(v), tensor_desc(slot_mapping)
-    dkc, dvc = tensor_desc(k_cache, k_scale), tensor_desc(v_cache, v_scale)
+    dk, dv, ds = _desc(k), _desc(v), _desc(slot_mapping)
+    dkc, dvc = _desc(k_cache, k_scale), _desc(v_cache, v_scale)
     _check(_lib.ak_store_kv(ctypes.byref(dk), ctypes.byref(dv), ctypes.byref(ds),
                             ctypes.byref(dkc), ctypes.byref(dvc), _stream_ptr(stream)))
 
@@ -321,9 +339,9 @@ def ak_run(plan: Plan, q, k_cache, v_cache, out=None, lse=None, k_scale: float =
 
     if out is None:
         out = torch.empty_like(q)
-    dq, dk, dv, do = (tensor_desc(q), tensor_desc(k_cache, k_scale), tensor_desc(v_cache, v_scale),
-                      tensor_desc(out))
-    dl = tensor_desc(lse) if lse is not None else None
+    dq, dk, dv, do = (_desc(q), _desc(k_cache, k_scale), _desc(v_cache, v_scale),
+                      _desc(out))
+    dl = _desc(lse) if lse is not None else None
     _check(_lib.ak_run(plan.handle, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                        ctypes.byref(do), ctypes.byref(dl) if dl is not None else None,
                        _stream_ptr(stream)))
@@ -340,8 +358,8 @@ def ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None)
         out = torch.empty_like(o_a)
     if lse_out is None:
         lse_out = torch.empty_like(lse_a)
-    da, dla, db, dlb, do, dlo = (tensor_desc(o_a), tensor_desc(lse_a), tensor_desc(o_b),
-                                 tensor_desc(lse_b), tensor_desc(out), tensor_desc(lse_out))
+    da, dla, db, dlb, do, dlo = (_desc(o_a), _desc(lse_a), _desc(o_b),
+                                 _desc(lse_b), _desc(out), _desc(lse_out))
     _check(_lib.ak_merge_states(ctypes.byref(da), ctypes.byref(dla), ctypes.byref(db),
                                 ctypes.byref(dlb), ctypes.byref(do), ctypes.byref(dlo),
                                 _stream_ptr(stream)))

@@ -58,3 +58,26 @@ def test_one_hip_runtime_per_process():
                        timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_cached_descriptors_match_fresh_ones():
+    # the entry points reuse descriptors keyed by everything a descriptor holds;
+    # for any tensor the cached one equals a freshly built one field by field
+    import torch
+
+    import paged_kv_attention_store_amd as ak
+
+    base = torch.zeros(6, 4, 8, 16, dtype=torch.bfloat16)
+    views = [base, base[:, :2], base[1:], base.permute(1, 0, 2, 3), base[..., :8],
+             base.view(24, 8, 16), torch.zeros(0, 3, dtype=torch.float32),
+             torch.zeros(5, dtype=torch.int64)]
+    for _ in range(2):                        # second pass: served from the cache
+        for v in views:
+            for scale in (1.0, 0.5):
+                a, b = ak._desc(v, scale), ak.tensor_desc(v, scale)
+                assert bytes(a) == bytes(b)
+    # a new tensor at a reused address with other strides gets its own descriptor
+    x = torch.zeros(8, 8)
+    d1 = bytes(ak._desc(x))
+    y = x.t()
+    assert bytes(ak._desc(y)) != d1 and bytes(ak._desc(y)) == bytes(ak.tensor_desc(y))
