@@ -186,3 +186,37 @@ def test_noncausal_more_queries_than_keys():
     eo, el, n = compare(wl, out, lse, -1, requests=keep)
     say(f"  rows={n} max|dout|={eo:.3e} max|dlse|={el:.3e}")
     assert eo <= TOL["bf16"][0] and el <= TOL["bf16"][1]
+
+
+def test_cascade_segments_on_two_streams():
+    # the shared segment on a side stream beside the suffix decode on the main
+    # stream, joined by an event before the merge: the same result
+    R, B, hq, hkv, D, k = 16, 16, 32, 8, 128, 32
+    rng = np.random.default_rng(5)
+    kl = rng.integers(k * B + 2, k * B + 900, size=R)
+    wl = W.custom(seed=41, q_lens=np.ones(R, np.int64), kv_lens=kl, page_size=B, num_qo_heads=hq,
+                  num_kv_heads=hkv, head_dim=D, name="cascade_2s")
+    for r in range(1, R):
+        wl.kv_indices[wl.kv_indptr[r]:wl.kv_indptr[r] + k] = wl.kv_indices[:k]
+    d = prepare(wl)
+    T = wl.total_q
+    shared = ak.ak_plan([0, T], [0, k], torch.from_numpy(wl.kv_indices[:k].copy()).cuda(), [B],
+                        hq, hkv, D, B, causal=False)
+    sx = np.concatenate([wl.kv_indices[wl.kv_indptr[r] + k:wl.kv_indptr[r + 1]] for r in range(R)])
+    si = np.concatenate([[0], np.cumsum(np.diff(wl.kv_indptr) - k)]).astype(np.int32)
+    suffix = ak.ak_plan(wl.qo_indptr, si, torch.from_numpy(sx.astype(np.int32)).cuda(),
+                        wl.last_page_len, hq, hkv, D, B)
+    side, main = torch.cuda.Stream(), torch.cuda.current_stream()
+    o1 = torch.empty_like(d["q"])
+    l1 = torch.empty(T, hq, device="cuda")
+    start = torch.cuda.Event()
+    start.record(main)
+    side.wait_event(start)
+    ak.ak_run(shared, d["q"], d["k_cache"], d["v_cache"], out=o1, lse=l1, stream=side)
+    done = torch.cuda.Event()
+    done.record(side)
+    o2, l2 = ak.ak_run(suffix, d["q"], d["k_cache"], d["v_cache"], lse=torch.empty(T, hq, device="cuda"))
+    main.wait_event(done)
+    out, lse = ak.ak_merge_states(o1, l1, o2, l2)
+    torch.cuda.synchronize()
+    check(wl, out, lse, -1)
