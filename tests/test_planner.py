@@ -85,8 +85,9 @@ class _FakeTensor:
     def data_ptr(self):
         return 16
 
-    def stride(self, i):
-        return (1024, 128, 1)[i]
+    def stride(self, i=None):
+        st = (1024, 128, 1)
+        return st if i is None else st[i]
 
 
 # --------------------------------------------------------------- coverage
