@@ -40,6 +40,7 @@ namespace {
 constexpr int kKB = 64;          // tokens per KV block
 constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
 constexpr int kDmaKB = 128;      // tokens per KV block of the bf16 (load-to-LDS) kernel
+constexpr int kLgkmcntZero = 0xC07F;   // s_waitcnt lgkmcnt(0), other counters unconstrained
 
 template <int D>
 __device__ __forceinline__ int k_pos(int t, int c) {
@@ -390,14 +391,11 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   const int hf = lane >> 5;
   const int G = a.G;
 
-  // ---- this lane's row
+  // ---- this lane's row (G is a power of two)
+  const int lgG = __builtin_ctz(G);
   const int rl = wave * 32 + n32;
   const bool rvalid = rl < it.nrows;
-  const int rho = it.row0 + rl;
-  const int jq = rho / G;
-  const int head = it.hk * G + (rho - jq * G);
-  const int64_t qtok = (int64_t)rq.q_off + jq;
-  const int qpos = rq.L - rq.n + jq;
+  const int qpos = rq.L - rq.n + ((it.row0 + rl) >> lgG);
   int row_lo = it.kv_begin, row_hi = it.kv_end;
   if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
   if (a.causal) row_hi = min(row_hi, qpos + 1);
@@ -415,14 +413,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   }
   const bool wave_active = (wave * 32) < it.nrows;
 
-  bf16x8 qop[NS];
-  {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + qtok * a.q_st + (int64_t)head * a.q_sh;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qop[s] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hf)
-                      : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-  }
+  bf16x8 qop[NS];   // read from LDS after the prologue
 
   f32x16 oacc[NDT];
 #pragma unroll
@@ -624,15 +615,52 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
     __syncthreads();
   };
 
-  // ---- prologue: block 0 copied, page ids of block 1 loaded (an empty KV range
-  // -- a non-causal request without pages -- has no blocks)
+  // ---- Q rows.  Each wave copies its 32 rows HBM -> LDS with the load-to-LDS path
+  // (whole rows per instruction, 16 bytes per lane), rows 0-15 into k1s and 16-31
+  // into v1s at the offset its own copy of block 1 will later fill, so no other
+  // wave touches them; chunk c of row r sits at slot c ^ (r mod CPR).  Rows past
+  // the tile's end fetch its last row (never stored).  Loaded by the lane that
+  // owns the row, a load instruction would touch 32 rows 32 bytes at a time.
+  static_assert(16 * 2 * D == NI * 1024, "a wave's Q half-tile fills its copy region");
+  auto issue_q = [&]() {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int o = 1024 * i + 16 * lane;             // byte within the half-tile
+        const int r = o / (2 * D), j = (o % (2 * D)) / 16;
+        const int rl_c = min(wave * 32 + 16 * pt + r, it.nrows - 1);
+        const int rho_c = it.row0 + rl_c;
+        const __bf16* src = static_cast<const __bf16*>(a.q) +
+                            ((int64_t)rq.q_off + (rho_c >> lgG)) * a.q_st +
+                            (int64_t)(it.hk * G + (rho_c & (G - 1))) * a.q_sh +
+                            8 * (j ^ (r & (CPR - 1)));
+        __bf16* dst = (pt ? v1s : k1s) + 512 * (wave * NI + i);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
+  };
+  auto read_q = [&]() {
+    const int r = n32 & 15;
+    const __bf16* qs = (n32 < 16 ? k1s : v1s) + 512 * wave * NI + r * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qop[s] = *reinterpret_cast<const bf16x8*>(qs + 8 * ((2 * s + hf) ^ (r & (CPR - 1))));
+  };
+
+  // ---- prologue: block 0 and the Q rows copied, page ids of block 1 loaded (an
+  // empty KV range -- a non-causal request without pages -- has no blocks)
   if (nb > 0) {
     load_pages(0, raw);
     issue_copy(k0s, v0s, 0, raw);
   }
+  issue_q();
   if (nb > 1) load_pages(1, raw);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  read_q();
+  // this wave's copy of block 1 lands on its Q rows: the reads complete first
+  __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
 
   for (int b = 0; b < nb; b += 2) {
     step(b, k0s, v0s, k1s, v1s);
@@ -642,35 +670,69 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 
   // ---- finalise: O^T element i of tile dt is column d = 32dt + 8(i/4) + 4hf + i%4
   const float l_tot = halves_sum(l_run);
-  if (!rvalid) return;
   const bool any = l_tot > 0.f;
   const float inv = any ? a.v_scale / l_tot : 0.f;
   const float lse2 = any ? m_run + log2f(l_tot) : -INFINITY;
+  // The row's addressing is recomputed here from a lane id the compiler cannot
+  // see through, so none of it is kept live (and spilled) across the block loop.
+  int le = __lane_id();
+  asm volatile("" : "+v"(le));
+  const int n32e = le & 31, hfe = le >> 5;
+  const int rle = wave * 32 + n32e;
+  const bool rvalide = rle < it.nrows;
+  const int rho = it.row0 + rle;
+  const int64_t qtok = (int64_t)rq.q_off + (rho >> lgG);
+  const int head = it.hk * G + (rho & (G - 1));
   if (it.pbase < 0) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + qtok * a.o_st + (int64_t)head * a.o_sh;
+    // Every wave is past the last block's barrier, so all LDS is free: wave w
+    // stages its 32 bf16 rows (padded by 16 bytes against bank conflicts) in its
+    // own slice, then stores whole rows, 16 bytes per lane and CPR lanes per row.
+    // Stored from the lane that owns the row, a store instruction would touch 32
+    // rows 8 bytes at a time.
+    constexpr int RS = 2 * D + 16;              // staged row stride in bytes
+    constexpr int RPI = 64 / CPR;               // rows per store instruction
+    static_assert(32 * RS <= TILE, "a wave's staged rows fit in its LDS slice");
+    __bf16* const arr = wave < 2 ? k0s : wave < 4 ? v0s : wave < 6 ? k1s : v1s;
+    char* const st = reinterpret_cast<char*>(arr) + (wave & 1) * TILE;   // TILE bytes = half an array
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
-        const u32x2 w{pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
-                      pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
+        const int d0 = 32 * dt + 8 * g + 4 * hfe;
+        *reinterpret_cast<u32x2*>(st + n32e * RS + 2 * d0) =
+            u32x2{pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                  pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
       }
-    if (a.lse && hf == 0) a.lse[qtok * a.l_st + (int64_t)head * a.l_sh] = lse2 * kLn2;
+    if (rvalide && a.lse && hfe == 0) a.lse[qtok * a.l_st + (int64_t)head * a.l_sh] = lse2 * kLn2;
+    __syncthreads();
+    const int c16 = le % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = i * RPI + le / CPR;        // row of the wave
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * RS + 16 * c16);
+      const int rl2 = wave * 32 + rr;
+      if (rl2 < it.nrows) {
+        const int rho2 = it.row0 + rl2;
+        const int head2 = it.hk * G + (rho2 & (G - 1));
+        uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)rq.q_off + (rho2 >> lgG)) * a.o_st +
+                       (int64_t)head2 * a.o_sh;
+        *reinterpret_cast<u32x4*>(op + 8 * c16) = v;
+      }
+    }
   } else {
-    const int64_t prow = (int64_t)it.pbase + rl;
+    if (!rvalide) return;
+    const int64_t prow = (int64_t)it.pbase + rle;
     float* pp = a.part_o + prow * D;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
+        const int d0 = 32 * dt + 8 * g + 4 * hfe;
         *reinterpret_cast<f32x4*>(pp + d0) =
             f32x4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
                   oacc[dt][4 * g + 3] * inv};
       }
-    if (hf == 0) a.part_lse[prow] = lse2;
+    if (hfe == 0) a.part_lse[prow] = lse2;
   }
 }
 
