@@ -3,9 +3,8 @@
 //
 // "vLLM attention backend", "Write the KV first": the step's K/V are written
 // into the paged cache by slot_mapping before attention reads the cache.
-// Memory-bound: each thread moves 8 consecutive elements of one (token, head)
-// row per iteration with 16-byte (or wider) vector accesses; K and V are the
-// two planes of blockIdx.y.
+// Memory-bound: one wave per token moves its row in 16-byte (or wider) vector
+// accesses; K and V are the two planes of blockIdx.y.
 
 #include "ak_launch.h"
 
@@ -79,30 +78,62 @@ struct Store8<AK_FP8_E4M3> {
 constexpr int elem_size(int dt) { return dt == AK_F32 ? 4 : (dt == AK_BF16 ? 2 : 1); }
 
 template <int SRC, int DST>
+__device__ __forceinline__ void move8(const char* sp, char* dp, float scale) {
+  float x[8];
+  Load8<SRC>::run(sp, x);
+  Store8<DST>::run(dp, x, scale);
+}
+
+// One wave per token: the token's slot is read once (a scalar load) and its
+// Hkv * D elements move as 8-element groups, 64 consecutive groups per
+// instruction, so every load and store instruction covers contiguous memory when
+// the token's heads are contiguous in both the source and the cache (the usual
+// layout); other head strides split the group index into (head, column).
+template <int SRC, int DST>
 __global__ __launch_bounds__(256) void store_kv_kernel(StoreArgs a) {
+  constexpr int ES = elem_size(SRC), ED = elem_size(DST);
   const int plane = blockIdx.y;
-  const int groups_per_head = a.D >> 3;
-  const int groups_per_tok = a.Hkv * groups_per_head;
-  const int64_t total = (int64_t)a.N * groups_per_tok;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gph = a.D >> 3;                  // groups per head
+  const int gpt = a.Hkv * gph;               // groups per token
+  const int64_t s_sh = a.s_sh[plane], d_sh = a.d_sh[plane];
+  const bool flat = s_sh == a.D && d_sh == a.D;
   const char* src = static_cast<const char*>(a.src[plane]);
   char* dst = static_cast<char*>(a.dst[plane]);
   const float scale = a.scale[plane];
-  for (int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gi < total;
-       gi += (int64_t)gridDim.x * blockDim.x) {
-    const int tok = (int)(gi / groups_per_tok);
-    const int rem = (int)(gi - (int64_t)tok * groups_per_tok);
-    const int h = rem / groups_per_head;
-    const int d0 = (rem - h * groups_per_head) << 3;
+  auto offs = [&](int j, int64_t& so, int64_t& dof) {
+    if (flat) {
+      so = dof = (int64_t)j << 3;
+    } else {
+      const int h = j / gph, d0 = (j - h * gph) << 3;
+      so = h * s_sh + d0;
+      dof = h * d_sh + d0;
+    }
+  };
+  for (int tok = blockIdx.x * 4 + wave; tok < a.N; tok += gridDim.x * 4) {
     const int64_t slot = a.slots[tok];
-    if (slot < 0 || slot >= a.num_slots) continue;
+    if (slot < 0 || slot >= a.num_slots) continue;   // uniform over the wave
     const int64_t page = slot / a.B;
     const int64_t off = slot - page * a.B;
-    const char* sp = src + (tok * a.s_st[plane] + h * a.s_sh[plane] + d0) * elem_size(SRC);
-    char* dp = dst + (page * a.d_sp[plane] + off * a.d_sb[plane] + h * a.d_sh[plane] + d0) *
-                         elem_size(DST);
-    float x[8];
-    Load8<SRC>::run(sp, x);
-    Store8<DST>::run(dp, x, scale);
+    const char* sp = src + (int64_t)tok * a.s_st[plane] * ES;
+    char* dp = dst + (page * a.d_sp[plane] + off * a.d_sb[plane]) * ED;
+    int j = lane;
+    for (; j + 64 < gpt; j += 128) {   // two groups in flight per lane
+      int64_t so0, do0, so1, do1;
+      offs(j, so0, do0);
+      offs(j + 64, so1, do1);
+      float x0[8], x1[8];
+      Load8<SRC>::run(sp + so0 * ES, x0);
+      Load8<SRC>::run(sp + so1 * ES, x1);
+      Store8<DST>::run(dp + do0 * ED, x0, scale);
+      Store8<DST>::run(dp + do1 * ED, x1, scale);
+    }
+    if (j < gpt) {
+      int64_t so, dof;
+      offs(j, so, dof);
+      move8<SRC, DST>(sp + so * ES, dp + dof * ED, scale);
+    }
   }
 }
 
@@ -142,8 +173,7 @@ hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hi
 
 hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s) {
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
-  const int64_t total = (int64_t)a.N * a.Hkv * (a.D >> 3);
-  int64_t blocks = (total + 255) / 256;
+  int64_t blocks = ((int64_t)a.N + 3) / 4;   // four tokens (waves) per block
   if (blocks > 8192) blocks = 8192;
   dim3 grid((unsigned)blocks, 2);
 #define AK_STORE_CASE(S, D)                                                 \
