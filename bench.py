@@ -22,6 +22,9 @@ the mixed chunked-prefill + decode step with full and sliding-window layers
 a 4096-token prefix run plainly (with the shared-pages flag, and streamed) and
 as a cascade ("cascade"), and a small
 decode batch issued eagerly and as a replayed graph over a fixed plan ("graph").
+Two optional legs measure the large-tile kernel alone: on long uniform prompts
+("prefill_shapes") and the fixed and per-block cost of a 256-row segment
+("segcost").
 
 The CPU baseline times the float64 oracle on a sample of the decode batch.
 """
@@ -463,6 +466,74 @@ def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup):
     return res
 
 
+def time_large(ak, torch, dev, wl, launches=20):
+    """Average duration (us) of the large-tile attention kernel on `wl`, HIP events
+    around every launch, two layers with their own caches alternating."""
+    layers = make_layers(wl, 2, dev)
+    idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
+    plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, wl.num_qo_heads,
+                      wl.num_kv_heads, wl.head_dim, wl.page_size, causal=wl.causal, window=-1)
+    for L in layers:
+        ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+    torch.cuda.synchronize()
+    ak.ak_profile_read()
+    ak.ak_profile_enable(True, kinds=["attn_large"])
+    for i in range(launches):
+        L = layers[i % 2]
+        ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
+    torch.cuda.synchronize()
+    ak.ak_profile_enable(False)
+    n, ms = ak.ak_profile_read()["attn_large"]
+    info = ak.ak_plan_info(plan)
+    del layers, plan
+    torch.cuda.empty_cache()
+    return ms / n * 1e3, info["large_items"]
+
+
+def measure_prefill_shapes(ak, torch, dev):
+    """Large-tile kernel TFLOP/s on long uniform prompts (the kernel's steady state,
+    against the ragged batch's short segments)."""
+    from synth import workloads as W
+    shapes = [
+        ("8 x 2048 over 4096 cached, page 1", W.custom(11, [2048] * 8, [6144] * 8, 1, 32, 8, 128)),
+        ("8 x 2048 over 4096 cached, page 16", W.custom(12, [2048] * 8, [6144] * 8, 16, 32, 8, 128)),
+        ("1 x 16384, page 16", W.custom(13, [16384], [16384], 16, 32, 8, 128)),
+        ("4 x 4096 non-causal, page 16",
+         W.custom(14, [4096] * 4, [4096] * 4, 16, 32, 8, 128, causal=False)),
+        ("8 x 1024, page 16", W.custom(15, [1024] * 8, [1024] * 8, 16, 32, 8, 128)),
+    ]
+    out = {}
+    for name, wl in shapes:
+        us, items = time_large(ak, torch, dev, wl)
+        flops = prefill_flops(wl, -1) if wl.causal else \
+            4.0 * wl.head_dim * wl.num_qo_heads * float(np.sum(wl.q_lens * wl.kv_lens))
+        out[name] = {"segments": items, "avg_launch_us": round(us, 1),
+                     "TFLOPs": round(flops / (us * 1e-6) / 1e12, 1)}
+        log(f"[bench] prefill shape {name}: {items} segments, {us:.1f} us, "
+            f"{out[name]['TFLOPs']} TFLOP/s")
+    return out
+
+
+def measure_segcost(ak, torch, dev, cus=256):
+    """Fixed and per-block cost of one 256-row segment: 256 requests of 64 new tokens
+    (one segment per KV head, 8 segments per compute unit) over KV lengths of k
+    blocks of 128 tokens, fitted as time per segment = fixed + k * per_block."""
+    from synth import workloads as W
+    ks, per_seg = [], []
+    for k in (1, 2, 4, 8, 16, 32):
+        wl = W.custom(20 + k, [64] * 256, [128 * k] * 256, 16, 32, 8, 128)
+        us, items = time_large(ak, torch, dev, wl)
+        ks.append(k)
+        per_seg.append(us / (items / cus))
+        log(f"[bench] segment cost: {k} blocks per segment, {items} segments, {us:.1f} us per launch, "
+            f"{per_seg[-1]:.2f} us per segment per CU")
+    A = np.vstack([np.ones(len(ks)), np.array(ks, float)]).T
+    (fixed, per_block), *_ = np.linalg.lstsq(A, np.array(per_seg), rcond=None)
+    log(f"[bench] segment cost fit: {fixed:.2f} us fixed + {per_block:.3f} us per block")
+    return {"blocks": ks, "us_per_segment_per_cu": [round(x, 2) for x in per_seg],
+            "fixed_us": round(float(fixed), 2), "per_block_us": round(float(per_block), 3)}
+
+
 WORKLOADS = {
     # name: (factory, layers with distinct caches)
     "prefill": (lambda W: W.config(3), 2),
@@ -470,6 +541,8 @@ WORKLOADS = {
     "longfp8": (lambda W: W.config(5), 4),
     "cascade": (lambda W: W.shared_prefix_decode(), 8),
     "graph": (lambda W: W.small_batch_decode(), 32),
+    "prefill_shapes": (None, 2),
+    "segcost": (None, 2),
 }
 
 
@@ -481,7 +554,7 @@ def main():
     ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
     ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph",
                     help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph "
-                         "('' for none)")
+                         "(default), prefill_shapes, segcost ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy timed as bandwidth context (0: skip)")
@@ -507,6 +580,12 @@ def main():
             continue
         if name == "graph":
             extra[name] = measure_graph(ak, torch, dev, fac(W), nl, max(5, args.steps), 3)
+            continue
+        if name == "prefill_shapes":
+            extra[name] = measure_prefill_shapes(ak, torch, dev)
+            continue
+        if name == "segcost":
+            extra[name] = measure_segcost(ak, torch, dev)
             continue
         extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
     cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
@@ -551,7 +630,7 @@ def main():
         "copy_GBs": copy,
     }
     for name, r in extra.items():
-        if name in ("cascade", "graph"):
+        if name in ("cascade", "graph", "prefill_shapes", "segcost"):
             line[name] = r
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
