@@ -1,5 +1,6 @@
 """store_kv on the GPU, bit-exact against the oracle's store (all five workloads,
-both readings of the tiny workload's store, every dtype conversion)."""
+both readings of the tiny workload's store, every dtype conversion, strided
+source and cache views)."""
 
 import numpy as np
 import pytest
@@ -45,6 +46,50 @@ def test_store_new_tokens_bit_exact(k):
         other = rng.choice(wl.pool_slots, size=min(2048, wl.pool_slots), replace=False)
         other = np.setdiff1d(other, slots)
         assert np.array_equal(_cache_rows(cache, other).view(np.uint8),
+                              oc.codes_at(other).view(np.uint8)), f"{w} pool rows differ"
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+@pytest.mark.parametrize("layout", ["fused_qkv", "head_pairs"])
+def test_store_strided_views_bit_exact(k, layout):
+    # Sources: K and V as slices of a fused [T, Hq + 2 Hkv, D] projection (token
+    # stride wider than a row, heads contiguous), or interleaved per head
+    # [T, Hkv, 2, D] (head stride 2 D).  Caches: K and V interleaved per head in
+    # one pool [P, B, Hkv, 2, D] (head stride 2 D), so the kernel's general
+    # (head, column) addressing runs, and the fused one on the sources.
+    wl = W.config(k)
+    say(f"[store] config {k}, strided views ({layout})")
+    d = prepare(wl, store_new=False)
+    P, B, H, D = d["k_cache"].shape
+    T = d["k_new"].shape[0]
+    if layout == "fused_qkv":
+        Hq = wl.num_qo_heads
+        fused = torch.empty(T, Hq + 2 * H, D, dtype=d["k_new"].dtype, device="cuda")
+        fused[:, Hq:Hq + H] = d["k_new"]
+        fused[:, Hq + H:] = d["v_new"]
+        ks, vs = fused[:, Hq:Hq + H], fused[:, Hq + H:]
+    else:
+        pairs = torch.empty(T, H, 2, D, dtype=d["k_new"].dtype, device="cuda")
+        pairs[:, :, 0] = d["k_new"]
+        pairs[:, :, 1] = d["v_new"]
+        ks, vs = pairs[:, :, 0], pairs[:, :, 1]
+    pool = torch.empty(P, B, H, 2, D, dtype=d["k_cache"].dtype, device="cuda")
+    pool[:, :, :, 0] = d["k_cache"]
+    pool[:, :, :, 1] = d["v_cache"]
+    kc, vc = pool[:, :, :, 0], pool[:, :, :, 1]
+    assert not ks.is_contiguous() and not kc.is_contiguous()
+    ak.ak_store_kv(ks, vs, d["slot_mapping"], kc, vc, wl.kv_scale, wl.kv_scale)
+    torch.cuda.synchronize()
+    okc, ovc = orun.caches_after_store(wl)
+    slots = wl.slot_mapping
+    rng = np.random.default_rng(100 + k)
+    other = np.setdiff1d(rng.choice(wl.pool_slots, size=min(2048, wl.pool_slots), replace=False),
+                         slots)
+    for w, cache, oc in (("k", kc, okc), ("v", vc, ovc)):
+        c = cache.contiguous()
+        assert np.array_equal(_cache_rows(c, slots).view(np.uint8),
+                              oc.codes_at(slots).view(np.uint8)), f"{w} new rows differ"
+        assert np.array_equal(_cache_rows(c, other).view(np.uint8),
                               oc.codes_at(other).view(np.uint8)), f"{w} pool rows differ"
 
 
