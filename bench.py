@@ -7,7 +7,9 @@ batch, then for each of the 32 layers ak_store_kv of the 64 new K/V rows into
 that layer's own cache followed by ak_run (split-KV decode + LSE merge).  All
 inputs are resident in HBM before the timed region.
 
-`value` = algorithmic HBM bytes of the step / step time (GB/s).  Algorithmic
+`value` = algorithmic HBM bytes of the step / step time (GB/s).
+`tokens_per_s_per_layer` = the step's new query tokens over the step time per
+layer (store, attention and merge; the plan amortised over the layers).  Algorithmic
 bytes per layer = visible KV rows (K and V) + Q + out + lse + page ids read,
 plus the store's reads and writes.  The roofline object reports the decode
 attention kernel alone: its algorithmic bytes per launch over its average
@@ -235,6 +237,8 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     flops = sum(prefill_flops(wl, w, large_only=True) for w in wins)
     step_bytes = sum(decode_bytes(wl, w) for w in wins) + n_layers * store_bytes(wl)
     res = dict(wl=wl, ms_step=ms_step, gbs=step_bytes / (ms_step * 1e-3) / 1e9, prof=prof,
+               tok_s_layer=wl.total_q / (ms_step * 1e-3 / n_layers),
+               dec_bytes=dec_bytes, flops=flops,
                info=ak.ak_plan_info(plans[0]), plan_us=plan_s / steps * 1e6,
                plan_host_us=plan_host_us,
                step_bytes=step_bytes, layers=n_layers)
@@ -247,6 +251,12 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     if n and flops:
         res["large_avg_ms"] = ms / n
         res["large_tflops"] = flops * steps / (ms * 1e-3) / 1e12
+    # both phases present: (bytes / HBM peak + flops / MFMA peak) over the measured
+    # attention time of a step
+    if "small_avg_ms" in res and "large_avg_ms" in res:
+        t_att = n_layers * (res["small_avg_ms"] + res["large_avg_ms"]) * 1e-3
+        res["combined_frac"] = (dec_bytes / (HBM_PEAK_GBS * 1e9) +
+                                flops / (BF16_PEAK_TFLOPS * 1e12)) / t_att
     n, ms = detail["store_kv"]
     if n:
         res["store_avg_us"] = ms / n * 1e3
@@ -628,6 +638,7 @@ def main():
         },
         "cpu_baseline": cpu,
         "copy_GBs": copy,
+        "tokens_per_s_per_layer": round(dec["tok_s_layer"], 1),
     }
     for name, r in extra.items():
         if name in ("cascade", "graph", "prefill_shapes", "segcost"):
@@ -635,7 +646,8 @@ def main():
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
              "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1),
-             "plan_host_us": round(r["plan_host_us"], 1)}
+             "plan_host_us": round(r["plan_host_us"], 1),
+             "tokens_per_s_per_layer": round(r["tok_s_layer"], 1)}
         if "small_gbs" in r:
             e["decode"] = {"kernel": "attn_small", "achieved": round(r["small_gbs"], 1),
                            "unit": "GB/s", "peak": HBM_PEAK_GBS,
@@ -650,6 +662,8 @@ def main():
             e["store_kv"] = {"GBs": round(r["store_gbs"], 1), "avg_us": round(r["store_avg_us"], 2)}
         if "merge_avg_us" in r:
             e["merge_avg_us"] = round(r["merge_avg_us"], 2)
+        if "combined_frac" in r:
+            e["combined_roofline_frac"] = round(r["combined_frac"], 4)
         line[name] = e
     print(json.dumps(line), flush=True)
 
