@@ -24,6 +24,12 @@ int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 
+// Guided decode split: a part aims at (decode KV still to cut) / (kGuideShare *
+// compute units) tokens (two per resident workgroup slot, two slots per compute
+// unit), at least chunk / kGuideFloor.
+constexpr int64_t kGuideShare = 4;
+constexpr int64_t kGuideFloor = 4;
+
 ak_status fail(ak_status s, const std::string& msg) {
   set_error(msg);
   return s;
@@ -153,8 +159,7 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
   chunk = std::max<int64_t>(chunk, min_chunk);
 
-  // Units longest first: their parts then come out in (nearly) decreasing size,
-  // so the tail of the grid holds the short items without sorting every item.
+  // Units longest first (partial rows and merge jobs follow this order).
   std::vector<int32_t> order(small.size());
   for (size_t i = 0; i < small.size(); ++i) order[i] = (int32_t)i;
   std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
@@ -165,22 +170,39 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
   int64_t prow = 0;
   int64_t split_units = 0;
+  // Guided part size: the units come longest first, and each is cut into parts of
+  // about (decode KV still to cut) / (kGuideShare * CUs) tokens, between
+  // chunk / kGuideFloor and chunk.  Parts shrink toward the end of the grid, so
+  // its last round holds short items and the compute units run out of work
+  // nearly together.
+  int64_t w_rem = small_tokens;
+  const int64_t t_floor = std::max<int64_t>(min_chunk, round_up(chunk / kGuideFloor, kKvAlign));
   for (int32_t ui : order) {
     const Unit& u = small[ui];
     const int64_t len = (int64_t)u.hi - u.lo;
-    int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, chunk)));
-    // boundaries on a kKvAlign grid anchored below lo
+    int64_t t = round_up(ceil_div(std::max<int64_t>(w_rem, 1), kGuideShare * (int64_t)p->num_cus), kKvAlign);
+    t = std::min<int64_t>(chunk, std::max<int64_t>(t, t_floor));
+    w_rem -= len;
+    // S parts with boundaries on a kKvAlign grid anchored below lo, each the grid
+    // point nearest to an equal share (parts differ by at most kKvAlign tokens;
+    // at least kKvAlign tokens per share keeps every part non-empty)
     const int64_t base = (u.lo / kKvAlign) * kKvAlign;
-    int64_t per, nparts;
+    const int64_t ext = (int64_t)u.hi - base;
+    int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, t)));
     for (;;) {
-      per = round_up(ceil_div((int64_t)u.hi - base, S), kKvAlign);
-      nparts = S <= 1 ? 1 : ceil_div((int64_t)u.hi - base, per);
+      S = std::max<int64_t>(1, std::min<int64_t>(S, ext / kKvAlign));
       // every part must fit a small tile's page table (only binds for tiny pages)
-      const int64_t span = nparts <= 1 ? (((int64_t)u.hi - 1) >> p->log2B) - (u.lo >> p->log2B) + 1
-                                       : (per + B - 1) / B + 1;
+      const int64_t span = S <= 1 ? (((int64_t)u.hi - 1) >> p->log2B) - (u.lo >> p->log2B) + 1
+                                  : (ceil_div(ext, S) + kKvAlign + B - 1) / B + 1;
       if (span <= kSmallMaxPages) break;
       S = std::max<int64_t>(S + 1, ceil_div(S * span, kSmallMaxPages - 1));
     }
+    const int64_t nparts = S;
+    auto bound = [&](int64_t s) -> int64_t {
+      if (s <= 0) return u.lo;
+      if (s >= nparts) return u.hi;
+      return std::max<int64_t>(u.lo, base + (s * ext + nparts * (kKvAlign / 2)) / (nparts * kKvAlign) * kKvAlign);
+    };
     if (nparts <= 1) {
       p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0, -1, {}});
       continue;
@@ -189,8 +211,8 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     // the unit's first merge job, which a part merging in-kernel starts from
     const int32_t m0 = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
     for (int64_t s = 0; s < nparts; ++s) {
-      const int32_t a = (int32_t)std::max<int64_t>(u.lo, base + s * per);
-      const int32_t b = (int32_t)std::min<int64_t>(u.hi, base + (s + 1) * per);
+      const int32_t a = (int32_t)bound(s);
+      const int32_t b = (int32_t)bound(s + 1);
       p->small_items.push_back(
           Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0, m0, {}});
     }
@@ -209,6 +231,14 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
   }
   p->small_merges = (int64_t)p->merges.size();
+  // Launch order: longest KV range first over all items (a unit's parts are equal
+  // slices of it, so unit order alone leaves long items behind short ones), so
+  // the dispatcher's earliest-free order approximates longest-processing-time
+  // scheduling and the grid ends on the shortest items.  Partial rows, merge jobs
+  // and arrival counters are indexed explicitly, so the order is free.
+  std::stable_sort(p->small_items.begin(), p->small_items.end(), [](const Item& x, const Item& y) {
+    return x.kv_end - x.kv_begin > y.kv_end - y.kv_begin;
+  });
   // ---- large tiles: one workgroup per segment, launched longest first so the
   // dispatcher's earliest-free-CU order approximates longest-processing-time
   // scheduling.  The cost of a segment is its 32-token KV tiles plus a fixed
@@ -317,11 +347,12 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
 
 // Bounds behind a fixed plan's workspace, following the planner above:
 //  * small units (<= kSmallRows rows) number at most Hkv * min(batch, tokens); a
-//    unit of len KV tokens gets at most ceil(len / chunk) parts, and the chunk is
-//    at least min_chunk and at least 1/(kPartsPerCu num_cus) of all small-unit KV (which is
-//    at most Hkv * pages * B), so all parts together number at most units +
-//    min(kPartsPerCu num_cus, Hkv pages B / min_chunk) (inside the guaranteed range the
-//    4096-token chunk cap and the page-table span never bind);
+//    unit of len KV tokens gets at most ceil(len / t) parts, where the guided part
+//    size t is at least min_chunk and at least chunk / kGuideFloor, and the chunk is
+//    at least 1/(kPartsPerCu num_cus) of all small-unit KV (which is at most
+//    Hkv * pages * B), so all parts together number at most units +
+//    min(kGuideFloor kPartsPerCu num_cus, Hkv pages B / min_chunk) (inside the
+//    guaranteed range the 4096-token chunk cap and the page-table span never bind);
 //  * large jobs number at most Hkv * (ceil(tokens G / kLargeRows) + requests with
 //    more than kSmallRows rows); splitting adds at most sum(t) / (share - kSegCost)
 //    segments, and share >= max(sum cost / num_cus, 2 kMinPartTiles + kSegCost)
@@ -337,7 +368,8 @@ void fixed_capacities(int32_t Hkv, int32_t G, int32_t B, int32_t num_cus, const 
   const int64_t rows_all = T * G * Hkv;               // unit rows over every KV head
   const int64_t units = (int64_t)Hkv * std::min<int64_t>(R, T);
   const int64_t kv_small = std::min<int64_t>(c->pages, INT64_MAX / (64 * 256)) * B * Hkv;
-  c->small = std::min<int64_t>(units * S, units + std::min<int64_t>((int64_t)kPartsPerCu * cus, ceil_div(kv_small, min_chunk)));
+  c->small = std::min<int64_t>(
+      units * S, units + std::min<int64_t>((int64_t)kGuideFloor * kPartsPerCu * cus, ceil_div(kv_small, min_chunk)));
   int64_t part_small = std::min<int64_t>((int64_t)kSmallRows * c->small, S * rows_all);
   int64_t merge_small = std::min<int64_t>((int64_t)kSmallRows * units, rows_all);
   if (c->small == 0) part_small = merge_small = 0;
