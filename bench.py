@@ -56,6 +56,7 @@ DECODE_KERNEL_SOURCES = [
     "paged_kv_attention_store_amd/csrc/ak_device.h",
     "paged_kv_attention_store_amd/csrc/ak_launch.h",
     "paged_kv_attention_store_amd/csrc/ak_internal.h",
+    "paged_kv_attention_store_amd/csrc/ak_plan.cpp",   # the split decides the partial traffic
     "paged_kv_attention_store_amd/build.py",
 ]
 
