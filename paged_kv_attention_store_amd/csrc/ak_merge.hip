@@ -7,7 +7,8 @@
 // output (fp32) and its LSE in base 2; the final LSE is written in base e.
 //
 // One wavefront per (query token, query head) job, each lane owning D/64
-// consecutive columns; bandwidth-bound (reads S * (D + 1) floats per job).
+// consecutive columns; bandwidth-bound (reads S * (D + 1) floats per job) once
+// the part loads overlap.
 // The same combination of two states given as tensors backs ak_merge_states.
 
 #include "ak_launch.h"
@@ -24,26 +25,46 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (job >= a.n_jobs) return;
   const MergeJob jb = a.jobs[job];
   if (jb.count == 0) return;   // padding job
+  // The parts' LSEs are read 64 at a time, one per lane, and reduced across the
+  // wave; lane j then holds part (chunk + j)'s weight, which the weighted sum
+  // takes by a lane broadcast.  The sum runs over the parts in order with four
+  // row loads in flight (the same arithmetic, part by part, as one load at a time).
   float m = -INFINITY;
-  for (int s = 0; s < jb.count; ++s) m = fmaxf(m, a.part_lse[jb.pfirst + (int64_t)s * jb.pstride]);
+  for (int s = lane; s < jb.count; s += 64) m = fmaxf(m, a.part_lse[jb.pfirst + (int64_t)s * jb.pstride]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
   float acc[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) acc[i] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < jb.count; ++s) {
-      const int64_t prow = jb.pfirst + (int64_t)s * jb.pstride;
-      const float w = exp2f(a.part_lse[prow] - m);   // -inf parts weigh 0
-      const float* po = a.part_o + prow * D + lane * PER;
-      if (PER == 2) {
-        const float2 v = *reinterpret_cast<const float2*>(po);
-        acc[0] += w * v.x;
-        acc[PER - 1] += w * v.y;
-      } else {
+    for (int c0 = 0; c0 < jb.count; c0 += 64) {
+      const int n = min(64, jb.count - c0);
+      const float wl = lane < n ? exp2f(a.part_lse[jb.pfirst + (int64_t)(c0 + lane) * jb.pstride] - m)
+                                : 0.f;   // -inf parts weigh 0
+      const float* pbase = a.part_o + ((int64_t)jb.pfirst + (int64_t)c0 * jb.pstride) * D + lane * PER;
+      const int64_t pstep = (int64_t)jb.pstride * D;
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        float v[4][PER];
 #pragma unroll
-        for (int i = 0; i < PER; ++i) acc[i] += w * po[i];
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int i = 0; i < PER; ++i) v[u][i] = pbase[(j + u) * pstep + i];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __shfl(wl, j + u, 64);
+#pragma unroll
+          for (int i = 0; i < PER; ++i) acc[i] += w * v[u][i];
+          wsum += w;
+        }
       }
-      wsum += w;
+      for (; j < n; ++j) {
+        const float w = __shfl(wl, j, 64);
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc[i] += w * pbase[j * pstep + i];
+        wsum += w;
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
