@@ -197,6 +197,50 @@ def test_over_planning_trap_is_a_hard_check():
 
 # ------------------------------------------------------- large-tile order
 
+# ------------------------------------------------------- decode split
+
+def _small(p):
+    items, _ = ak.ak_plan_export(p)
+    info = ak.ak_plan_info(p)
+    return items[:info["small_items"]], info
+
+
+@pytest.mark.parametrize("k", [2, 4, 5])
+@pytest.mark.parametrize("num_cus", [64, 256])
+def test_decode_parts_longest_first_even_and_bounded(k, num_cus):
+    # decode items launch longest KV range first; a unit's parts tile its visible
+    # range without gaps, none empty, sizes within two 64-token grid steps of each
+    # other (the first part is shorter by the unit's offset from the grid); the
+    # count respects the fixed-plan bound units + 4 * 6 * num_cus where that bound
+    # is stated (decode KV <= 6 * num_cus * 4096 tokens over the KV heads), and
+    # units + KV / 1024 (parts of at least a quarter of the 4096-token chunk cap)
+    # beyond it
+    wl = W.config(k)
+    for w in wl.windows:
+        p = host_plan(wl.qo_indptr, wl.kv_indptr, wl.last_page_len, hq=wl.num_qo_heads,
+                      hkv=wl.num_kv_heads, B=wl.page_size, causal=True, window=w, num_cus=num_cus)
+        small, info = _small(p)
+        ln = small[:, 5] - small[:, 4]
+        assert np.all(ln > 0) and np.all(np.diff(ln) <= 0)
+        units = {}
+        for it in small:
+            units.setdefault((int(it[0]), int(it[1])), []).append((int(it[4]), int(it[5])))
+        for (r, hk), parts in units.items():
+            parts.sort()
+            assert all(parts[i][1] == parts[i + 1][0] for i in range(len(parts) - 1))
+            L, n = int(wl.kv_lens[r]), int(wl.q_lens[r])
+            hi = L if n > 0 else 0
+            lo = 0 if w < 0 else max(0, L - n - w)
+            assert parts[0][0] == lo and parts[-1][1] == hi
+            sizes = [b - a for a, b in parts]
+            assert max(sizes) - min(sizes) <= 128, (r, hk, sizes)
+        kv = sum(b - a for parts in units.values() for a, b in parts)
+        if kv <= 6 * num_cus * 4096:
+            assert len(small) <= len(units) + 4 * 6 * num_cus
+        else:
+            assert len(small) <= len(units) + -(-kv // 1024)
+
+
 def _large(p):
     items, _ = ak.ak_plan_export(p)
     info = ak.ak_plan_info(p)
