@@ -69,6 +69,8 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   p->G = G;
   p->log2B = 0;
   while ((1 << p->log2B) < B) ++p->log2B;
+  int lgG = 0;   // G is a power of two (validated above)
+  while ((1 << lgG) < G) ++lgG;
   p->causal = causal;
   p->window = window;
   p->num_cus = num_cus > 0 ? num_cus : 256;
@@ -166,7 +168,10 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const int32_t lx = small[x].hi - small[x].lo, ly = small[y].hi - small[y].lo;
     return lx != ly ? lx > ly : x < y;
   });
-  p->small_items.reserve(small.size() + (size_t)(small_tokens / chunk) + 16);
+  p->merges.reserve((size_t)small.size() * kSmallRows);
+  // parts are at least chunk / kGuideFloor tokens (or min_chunk)
+  p->small_items.reserve(small.size() +
+                         (size_t)(small_tokens / std::max<int64_t>(min_chunk, chunk / kGuideFloor)) + 16);
 
   int64_t prow = 0;
   int64_t split_units = 0;
@@ -210,17 +215,18 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const int64_t ubase = prow;
     // the unit's first merge job, which a part merging in-kernel starts from
     const int32_t m0 = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
+    int32_t a = (int32_t)bound(0);
     for (int64_t s = 0; s < nparts; ++s) {
-      const int32_t a = (int32_t)bound(s);
       const int32_t b = (int32_t)bound(s + 1);
       p->small_items.push_back(
           Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0, m0, {}});
+      a = b;
     }
     const Req& q = p->reqs[u.r];
     for (int32_t rho = 0; rho < u.rows; ++rho) {
       MergeJob m{};
-      m.token = q.q_off + rho / G;
-      m.head = u.hk * G + rho % G;
+      m.token = q.q_off + (rho >> lgG);
+      m.head = u.hk * G + (rho & (G - 1));
       m.pfirst = (int32_t)(ubase + rho);
       m.pstride = u.rows;
       m.count = (int32_t)nparts;
@@ -236,9 +242,29 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
   // the dispatcher's earliest-free order approximates longest-processing-time
   // scheduling and the grid ends on the shortest items.  Partial rows, merge jobs
   // and arrival counters are indexed explicitly, so the order is free.
-  std::stable_sort(p->small_items.begin(), p->small_items.end(), [](const Item& x, const Item& y) {
-    return x.kv_end - x.kv_begin > y.kv_end - y.kv_begin;
-  });
+  {
+    // a stable counting sort by length when the lengths span a short range (the
+    // usual case: parts are at most the 4096-token chunk), else a comparison sort
+    const size_t n = p->small_items.size();
+    int32_t lmax = 0;
+    for (const Item& x : p->small_items) lmax = std::max(lmax, x.kv_end - x.kv_begin);
+    std::vector<Item> sorted(n);
+    if ((size_t)lmax <= 4 * n + 65536) {
+      std::vector<int32_t> start((size_t)lmax + 2, 0);
+      for (const Item& x : p->small_items) ++start[(size_t)(lmax - (x.kv_end - x.kv_begin)) + 1];
+      for (size_t k = 1; k < start.size(); ++k) start[k] += start[k - 1];
+      for (const Item& x : p->small_items) sorted[(size_t)start[(size_t)(lmax - (x.kv_end - x.kv_begin))]++] = x;
+    } else {
+      std::vector<uint64_t> key(n);
+      for (size_t i = 0; i < n; ++i) {
+        const Item& x = p->small_items[i];
+        key[i] = ((uint64_t)(uint32_t)(lmax - (x.kv_end - x.kv_begin)) << 32) | (uint64_t)i;
+      }
+      std::sort(key.begin(), key.end());
+      for (size_t i = 0; i < n; ++i) sorted[i] = p->small_items[(size_t)(key[i] & 0xFFFFFFFFu)];
+    }
+    p->small_items.swap(sorted);
+  }
   // ---- large tiles: one workgroup per segment, launched longest first so the
   // dispatcher's earliest-free-CU order approximates longest-processing-time
   // scheduling.  The cost of a segment is its 32-token KV tiles plus a fixed
@@ -308,8 +334,8 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       for (int32_t rl = 0; rl < j.nrows; ++rl) {
         const int32_t rho = j.row0 + rl;
         MergeJob m{};
-        m.token = q.q_off + rho / G;
-        m.head = j.hk * G + rho % G;
+        m.token = q.q_off + (rho >> lgG);
+        m.head = j.hk * G + (rho & (G - 1));
         m.pfirst = (int32_t)(prow + rl);
         m.pstride = j.nrows;
         m.count = nparts[i];
