@@ -305,3 +305,49 @@ def test_noncausal_allows_more_queries_than_keys():
     # the request without pages is still planned (its rows get the empty state)
     assert set(items[:, 0].tolist()) == {0, 1, 2}
     assert np.all(items[items[:, 0] == 1][:, 4:6] == 0)
+
+
+# ------------------------------------------------------- host threads
+
+def test_concurrent_planning_from_threads():
+    # plans made from eight host threads at once (the calls release the GIL) equal
+    # the ones made alone, and each thread's error message is its own
+    import threading
+    cases = []
+    for k in (1, 2, 3, 4):
+        wl = W.config(k)
+        cases.append((wl.qo_indptr, wl.kv_indptr, wl.last_page_len, wl.num_qo_heads,
+                      wl.num_kv_heads, wl.head_dim, wl.page_size))
+    ref = []
+    for qo, kv, last, hq, hkv, d, B in cases:
+        items, lens = ak.ak_plan_export(host_plan(qo, kv, last, hq=hq, hkv=hkv, d=d, B=B))
+        ref.append((items.copy(), lens.copy()))
+    errors = []
+
+    def worker(tid):
+        try:
+            for it in range(12):
+                c = (tid + it) % len(cases)
+                qo, kv, last, hq, hkv, d, B = cases[c]
+                if it % 3 == 2:   # a bad request of this thread's own making
+                    bad = np.array(last, dtype=np.int32).copy()
+                    bad[0] = B + 1 + tid
+                    try:
+                        host_plan(qo, kv, bad, hq=hq, hkv=hkv, d=d, B=B)
+                        errors.append((tid, "accepted a bad last_page_len"))
+                    except ak.AkError as e:
+                        if e.status != ak.AK_ERR_BAD_LENGTHS or f"= {B + 1 + tid} " not in str(e):
+                            errors.append((tid, str(e)))
+                    continue
+                items, lens = ak.ak_plan_export(host_plan(qo, kv, last, hq=hq, hkv=hkv, d=d, B=B))
+                if not (np.array_equal(items, ref[c][0]) and np.array_equal(lens, ref[c][1])):
+                    errors.append((tid, f"work list of case {c} differs"))
+        except Exception as e:   # noqa: BLE001 - reported below
+            errors.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:4]
