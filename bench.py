@@ -513,6 +513,9 @@ def measure_prefill_shapes(ak, torch, dev):
          W.custom(14, [4096] * 4, [4096] * 4, 16, 32, 8, 128, causal=False)),
         ("8 x 1024, page 16", W.custom(15, [1024] * 8, [1024] * 8, 16, 32, 8, 128)),
     ]
+    r3 = W.config(3)
+    shapes.append(("ragged prefill batch, fp8 caches, page 16",
+                   W.custom(16, r3.q_lens, r3.kv_lens, 16, 32, 8, 128, kv_dtype="fp8")))
     out = {}
     for name, wl in shapes:
         us, items = time_large(ak, torch, dev, wl)

@@ -7,29 +7,18 @@
 // come from" (causal bit and window_left, never a materialised mask); the GQA
 // head-group fusion figure of "Why metadata is built once per step".
 //
-// gfx950 mapping.  One workgroup of 8 waves per 256-row tile, wave w owning rows
-// 32w .. 32w+31 (one workgroup per CU, <= 256 registers per lane, 66 KB of LDS).
-// The KV range is walked in 64-token blocks with a software pipeline:
-//   * block i+1's K rows (waves 4-7) and V rows (waves 0-3) are loaded into
-//     registers while block i is computed from LDS, then written into the other
-//     LDS buffer (one barrier per block); the page ids of block i+2 are fetched
-//     one iteration earlier still.  256 rows per tile give each loaded K/V byte
-//     twice the MFMA work of a 128-row tile, and twice the compute to hide the
-//     next block's gather behind;
-//   * K is staged as 16-byte chunks XOR-swizzled by token (conflict-free MFMA
-//     operand reads); V is staged transposed (d-major, 4-token groups swizzled
-//     by d) so a PV operand is two 8-byte reads;
-//   * each 32-token half of a block goes through S^T (32 tokens x 32 rows) =
-//     K Q^T (32x32x16 bf16 MFMA, Q in registers), softmax and PV before the
-//     next half, so one S accumulator is live at a time (no register spills);
-//   * softmax in base 2 with the scale folded into one FMA per score; a row lives
-//     in lanes n and n+32 (one xor-shuffle for its max); masks are applied only
-//     on tiles that cross a row's causal or window bound;
-//   * the running max is raised only when a tile exceeds it by more than 2^8
-//     (the normalisation is exact for any reference value; this only skips
-//     rescaling O, and probabilities stay below 2^8);
-//   * O^T (D x 32 rows) += V^T P^T, P taken from the S^T registers as produced.
-// FP8 caches are widened to bf16 while staging (exact).
+// gfx950 mapping.  One workgroup of 8 waves per 256-row segment, wave w owning
+// rows 32w .. 32w+31 (one workgroup per CU: <= 256 registers per lane, up to
+// 128 KB of LDS).  The KV range is walked in 128-token blocks whose K and V rows
+// are copied HBM -> LDS by the load-to-LDS path while the previous block is
+// computed (bf16 caches straight into the compute layout; fp8 caches into a
+// staging buffer, widened exactly to bf16 once per block).  Per block and 32-token
+// tile: S^T = K Q^T and O^T += V^T P^T on the 32x32x16 bf16 MFMA with Q in
+// registers, online softmax in base 2 with the scale folded into one FMA per
+// score, the running max raised only when a tile exceeds it by more than 2^8
+// (the normalisation is exact for any reference value; this only skips rescaling
+// O, and probabilities stay below 2^8).  The kernels' own comments give the
+// layouts.
 
 #include "ak_launch.h"
 
@@ -37,304 +26,9 @@ namespace ak {
 
 namespace {
 
-constexpr int kKB = 64;          // tokens per KV block
 constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
 constexpr int kDmaKB = 128;      // tokens per KV block of the bf16 (load-to-LDS) kernel
 constexpr int kLgkmcntZero = 0xC07F;   // s_waitcnt lgkmcnt(0), other counters unconstrained
-
-template <int D>
-__device__ __forceinline__ int k_pos(int t, int c) {
-  // position of 16-byte chunk c of token t's K row in the staged tile (in chunks)
-  return t * (D / 8) + (D == 128 ? (c ^ (t & 15)) : (c ^ ((t >> 1) & 7)));
-}
-
-__device__ __forceinline__ int vt_pos(int d, int tg) {
-  // position (in bf16) of 4-token group tg of column d in the transposed V tile
-  return d * kKB + ((tg ^ (d & 15)) << 2);
-}
-
-template <int D, bool FP8>
-__global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
-  constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
-  constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
-  constexpr int CPR = D / 8;                  // 16-byte bf16 chunks per row
-  constexpr int SCPR = FP8 ? CPR / 2 : CPR;   // 16-byte source chunks per row
-  constexpr int KLD = kKB * SCPR / 256;       // K source chunks per K-loader thread per block
-  constexpr int VPAIRS = (kKB / 4) * CPR;     // (4-token group, 8-column chunk) pairs
-  static_assert(KLD >= 1 && KLD <= 4 && VPAIRS <= 256, "tile shape");
-  __shared__ __align__(16) __bf16 ks[2][kKB * D];
-  __shared__ __align__(16) __bf16 vt[2][D * kKB];
-  __shared__ int64_t s_koff[2][kKB], s_voff[2][kKB];
-
-  const Item it = a.items[blockIdx.x];
-  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
-  const Req rq = a.reqs[it.r];
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int n32 = lane & 31;
-  const int hf = lane >> 5;
-  const int G = a.G;
-
-  // ---- this lane's row
-  const int rl = wave * 32 + n32;
-  const bool rvalid = rl < it.nrows;
-  const int rho = it.row0 + rl;
-  const int jq = rho / G;
-  const int head = it.hk * G + (rho - jq * G);
-  const int64_t qtok = (int64_t)rq.q_off + jq;
-  const int qpos = rq.L - rq.n + jq;
-  int row_lo = it.kv_begin, row_hi = it.kv_end;
-  if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
-  if (a.causal) row_hi = min(row_hi, qpos + 1);
-  if (!rvalid) row_lo = row_hi = 0;
-  // blocks entirely inside [wave_lo_max, wave_hi_min) need no mask
-  int wave_lo_max = row_lo, wave_hi_min = row_hi;
-#pragma unroll
-  for (int k = 32; k >= 1; k >>= 1) {
-    wave_lo_max = max(wave_lo_max, __shfl_xor(wave_lo_max, k, 64));
-    wave_hi_min = min(wave_hi_min, __shfl_xor(wave_hi_min, k, 64));
-  }
-  const bool wave_active = (wave * 32) < it.nrows;
-
-  bf16x8 qop[NS];
-  {
-    const __bf16* qp = static_cast<const __bf16*>(a.q) + qtok * a.q_st + (int64_t)head * a.q_sh;
-#pragma unroll
-    for (int s = 0; s < NS; ++s)
-      qop[s] = rvalid ? *reinterpret_cast<const bf16x8*>(qp + 16 * s + 8 * hf)
-                      : __builtin_bit_cast(bf16x8, u32x4{0, 0, 0, 0});
-  }
-
-  f32x16 oacc[NDT];
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.score_scale;
-
-  const int ebytes = FP8 ? 1 : 2;
-  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * ebytes;
-  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * ebytes;
-  const int32_t bmask = (1 << a.log2B) - 1;
-  const int nb = (it.kv_end - it.kv_begin + kKB - 1) / kKB;
-
-  // page id of this lane's token in block b (wave 0 only), clamped into the range
-  auto page_of = [&](int b) -> int64_t {
-    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
-    return kv_page(a.kv_indices, rq.page_off, t, a.log2B, a.num_pages);
-  };
-  auto put_offsets = [&](int b, int64_t page, int buf) {
-    const int t = min(it.kv_begin + b * kKB + lane, it.kv_end - 1);
-    const int64_t slot = t & bmask;
-    s_koff[buf][lane] = (page * a.k_sp + slot * a.k_sb) * ebytes;
-    s_voff[buf][lane] = (page * a.v_sp + slot * a.v_sb) * ebytes;
-  };
-
-  // prefetch registers: waves 4-7 hold K source chunks, waves 0-3 the V rows of
-  // one (4-token group, 8-column chunk) pair
-  u32x4 pre[4];
-  const bool k_loader = wave >= 4;
-  const int lt = tid & 255;                  // index among the 256 loaders of a kind
-  const int vu = lt & 15, vc = lt >> 4;      // V pair (valid if lt < VPAIRS)
-  auto load_block = [&](int buf) {
-    if (k_loader) {
-#pragma unroll
-      for (int k = 0; k < KLD; ++k) {
-        const int q = lt + 256 * k;
-        const int t = q / SCPR, cc = q % SCPR;
-        pre[k] = *reinterpret_cast<const u32x4*>(kbase + s_koff[buf][t] + cc * 16);
-      }
-    } else if (lt < VPAIRS) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const char* src = vbase + s_voff[buf][4 * vu + j];
-        if (FP8) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(src + vc * 8);
-          pre[j] = u32x4{w[0], w[1], 0u, 0u};
-        } else {
-          pre[j] = *reinterpret_cast<const u32x4*>(src + vc * 16);
-        }
-      }
-    }
-  };
-  auto store_block = [&](int buf) {
-    if (k_loader) {
-#pragma unroll
-      for (int k = 0; k < KLD; ++k) {
-        const int q = lt + 256 * k;
-        const int t = q / SCPR, cc = q % SCPR;
-        if (FP8) {
-          *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc)]) =
-              e4m3x8_to_bf16x8(pre[k][0], pre[k][1]);
-          *reinterpret_cast<bf16x8*>(&ks[buf][8 * k_pos<D>(t, 2 * cc + 1)]) =
-              e4m3x8_to_bf16x8(pre[k][2], pre[k][3]);
-        } else {
-          *reinterpret_cast<u32x4*>(&ks[buf][8 * k_pos<D>(t, cc)]) = pre[k];
-        }
-      }
-    } else if (lt < VPAIRS) {
-      uint32_t e[4][4];   // e[token][dword]: bf16 pairs of columns 8vc .. 8vc+7
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (FP8) {
-          const u32x4 b = __builtin_bit_cast(u32x4, e4m3x8_to_bf16x8(pre[j][0], pre[j][1]));
-#pragma unroll
-          for (int k = 0; k < 4; ++k) e[j][k] = b[k];
-        } else {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) e[j][k] = pre[j][k];
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int d = 8 * vc + i;
-        uint32_t lo, hi;
-        if (i & 1) {
-          lo = __builtin_amdgcn_perm(e[1][i >> 1], e[0][i >> 1], 0x07060302u);
-          hi = __builtin_amdgcn_perm(e[3][i >> 1], e[2][i >> 1], 0x07060302u);
-        } else {
-          lo = __builtin_amdgcn_perm(e[1][i >> 1], e[0][i >> 1], 0x05040100u);
-          hi = __builtin_amdgcn_perm(e[3][i >> 1], e[2][i >> 1], 0x05040100u);
-        }
-        *reinterpret_cast<u32x2*>(&vt[buf][vt_pos(d, vu)]) = u32x2{lo, hi};
-      }
-    }
-  };
-
-  // ---- prologue: offsets of blocks 0 and 1, block 0 staged, page ids of block 2 in flight
-  // (an empty KV range -- a non-causal request without pages -- has no blocks)
-  int64_t page_next = 0;
-  if (nb > 0 && wave == 0) {
-    put_offsets(0, page_of(0), 0);
-    if (nb > 1) put_offsets(1, page_of(1), 1);
-    if (nb > 2) page_next = page_of(2);
-  }
-  __syncthreads();
-  if (nb > 0) {
-    load_block(0);
-    store_block(0);
-  }
-  __syncthreads();
-
-  for (int b = 0; b < nb; ++b) {
-    const int cur = b & 1;
-    const int tb = it.kv_begin + b * kKB;
-    if (b + 1 < nb) load_block(cur ^ 1);   // lands while this block is computed
-
-    if (wave_active) {
-      // two 32-token tiles, each through S^T, softmax and PV before the next
-      // (one S accumulator live at a time)
-#pragma unroll
-      for (int T = 0; T < 2; ++T) {
-        // ---- S^T = K Q^T for tokens 32T .. 32T+31 of the block
-        f32x16 sacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
-        const int t = 32 * T + n32;
-#pragma unroll
-        for (int s = 0; s < NS; ++s) {
-          const bf16x8 kop =
-              *reinterpret_cast<const bf16x8*>(&ks[cur][8 * k_pos<D>(t, 2 * s + hf)]);
-          sacc = mfma32(kop, qop[s], sacc);
-        }
-        // ---- mask (tiles crossing a row bound only); element i is token 32T + 8(i/4) + 4hf + i%4
-        const int tt0 = tb + 32 * T;
-        if ((tt0 < wave_lo_max) | (tt0 + 32 > wave_hi_min)) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
-          }
-        }
-        float mb = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
-        mb = fmaxf(mb, shfl_xor_f(mb, 32)) * c;       // tile max in base-2 units
-        // raise the reference max only when the tile exceeds it by kLazy
-        const float m_new = (mb > m_run + kLazy) ? mb : m_run;
-        if (__any(m_new != m_run)) {
-          // rows whose reference stays put keep alpha = 1 (this also covers rows that
-          // have seen no visible key yet: -inf - -inf would be NaN); a row leaving
-          // -inf gets exp2(-inf) = 0
-          const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
-          m_run = m_new;
-        }
-        const float msub = m_run == -INFINITY ? 0.f : m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          sacc[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
-          psum += sacc[i];
-        }
-        l_run += psum;
-        // ---- O^T += V^T P^T over the tile's two 16-token k-steps
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const int kk = 2 * T + kh, i0 = 8 * kh;
-          u32x4 pw;
-#pragma unroll
-          for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(sacc[i0 + 2 * h], sacc[i0 + 2 * h + 1]);
-          const bf16x8 pop = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const int d = 32 * dt + n32;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + hf)]);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(&vt[cur][vt_pos(d, 4 * kk + 2 + hf)]);
-            const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-            oacc[dt] = mfma32(vop, pop, oacc[dt]);
-          }
-        }
-      }
-    }
-
-    if (b + 1 < nb) store_block(cur ^ 1);
-    if (wave == 0 && b + 2 < nb) {
-      put_offsets(b + 2, page_next, cur);        // block b's offsets are no longer read
-      if (b + 3 < nb) page_next = page_of(b + 3);
-    }
-    __syncthreads();
-  }
-
-  // ---- finalise: O^T element i of tile dt is column d = 32dt + 8(i/4) + 4hf + i%4
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
-  if (!rvalid) return;
-  const bool any = l_tot > 0.f;
-  const float inv = any ? a.v_scale / l_tot : 0.f;
-  const float lse2 = any ? m_run + log2f(l_tot) : -INFINITY;
-  if (it.pbase < 0) {
-    uint16_t* op = static_cast<uint16_t*>(a.out) + qtok * a.o_st + (int64_t)head * a.o_sh;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
-        const u32x2 w{pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
-                      pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + d0) = w;
-      }
-    if (a.lse && hf == 0) a.lse[qtok * a.l_st + (int64_t)head * a.l_sh] = lse2 * kLn2;
-  } else {
-    const int64_t prow = (int64_t)it.pbase + rl;
-    float* pp = a.part_o + prow * D;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hf;
-        *reinterpret_cast<f32x4*>(pp + d0) =
-            f32x4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
-                  oacc[dt][4 * g + 3] * inv};
-      }
-    if (hf == 0) a.part_lse[prow] = lse2;
-  }
-}
 
 // ---------------------------------------------------------------------------
 // bf16 caches: K and V tiles are copied HBM -> LDS by the load-to-LDS path
@@ -737,6 +431,408 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 }
 
 
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3 caches: the same kernel with the K/V rows copied HBM -> LDS as fp8
+// (half the bytes) and widened exactly to bf16 in LDS once per block, ahead of the
+// bf16 kernel's tile loop (one more barrier per block); the scales are folded
+// into the score scale and 1/l as for every fp8 path.
+
+template <int D, int KB>
+__global__ __launch_bounds__(512, 2) void attn_large_dma8_kernel(AttnArgs a) {
+  constexpr int NS = D / 16;                  // S^T k-steps (16 d each)
+  constexpr int NDT = D / 32;                 // O^T d-tiles (32 d each)
+  constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  constexpr int NT = KB / 32;                 // 32-token tiles per block
+  constexpr int TILE = KB * D;                // bf16 elements of one K or V block
+  constexpr int NI = KB * CPR / (64 * 8);     // load-to-LDS instructions per wave per block
+  static_assert(NI >= 1 && NI * 64 * 8 == KB * CPR, "tile shape");
+  constexpr int CPR8 = D / 16;                // 16-byte chunks per fp8 row
+  constexpr int NI8 = KB * CPR8 / (64 * 8);   // fp8 copy instructions per wave per block
+  static_assert(NI8 >= 1 && NI8 * 64 * 8 == KB * CPR8, "fp8 tile shape");
+  __shared__ __align__(16) __bf16 kb[TILE];      // the block's K widened to bf16 (compute layout)
+  __shared__ __align__(16) __bf16 vb[TILE];      // the block's V widened to bf16
+  __shared__ __align__(16) uint8_t k8a[KB * D];  // fp8 K/V copies, double-buffered
+  __shared__ __align__(16) uint8_t k8b[KB * D];
+  __shared__ __align__(16) uint8_t v8a[KB * D];
+  __shared__ __align__(16) uint8_t v8b[KB * D];
+
+  const Item it = a.items[blockIdx.x];
+  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
+  const Req rq = a.reqs[it.r];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int n32 = lane & 31;
+  const int hf = lane >> 5;
+  const int G = a.G;
+
+  // ---- this lane's row (G is a power of two)
+  const int lgG = __builtin_ctz(G);
+  const int rl = wave * 32 + n32;
+  const bool rvalid = rl < it.nrows;
+  const int qpos = rq.L - rq.n + ((it.row0 + rl) >> lgG);
+  int row_lo = it.kv_begin, row_hi = it.kv_end;
+  if (a.window >= 0) row_lo = max(row_lo, qpos - a.window);
+  if (a.causal) row_hi = min(row_hi, qpos + 1);
+  if (!rvalid) row_lo = row_hi = INT_MIN;       // sees nothing; neutral in the bounds below
+  // [lo_max, hi_min): every valid row of the wave sees it (no mask needed);
+  // outside [lo_min, hi_max): no row of the wave sees it (nothing to compute)
+  int lo_max = rvalid ? row_lo : INT_MIN, hi_min = rvalid ? row_hi : INT_MAX;
+  int lo_min = rvalid ? row_lo : INT_MAX, hi_max = rvalid ? row_hi : INT_MIN;
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) {
+    lo_max = max(lo_max, __shfl_xor(lo_max, k, 64));
+    hi_min = min(hi_min, __shfl_xor(hi_min, k, 64));
+    lo_min = min(lo_min, __shfl_xor(lo_min, k, 64));
+    hi_max = max(hi_max, __shfl_xor(hi_max, k, 64));
+  }
+  const bool wave_active = (wave * 32) < it.nrows;
+
+  bf16x8 qop[NS];   // read from LDS after the prologue
+
+  f32x16 oacc[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[dt][i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = a.score_scale;
+
+  const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh;
+  const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh;
+  const int32_t bmask = (1 << a.log2B) - 1;
+  const int nb = (it.kv_end - it.kv_begin + KB - 1) / KB;
+
+  // The fp8 copy of a block is NI8 load-to-LDS instructions per wave for K and NI8
+  // for V; lane l of instruction i carries chunk q = (wave*NI8 + i)*64 + l of the
+  // block (token q / CPR8), into the staging buffer as it sits in the cache row.
+  // Each wave loads the page ids of its own tokens one block ahead of the copy.
+  auto copy_token = [&](int b, int i) {
+    return min(it.kv_begin + b * KB + ((wave * NI8 + i) * 64 + lane) / CPR8, it.kv_end - 1);
+  };
+  auto load_pages = [&](int b, int32_t (&raw)[NI8]) {
+#pragma unroll
+    for (int i = 0; i < NI8; ++i) raw[i] = a.kv_indices[rq.page_off + (copy_token(b, i) >> a.log2B)];
+  };
+  const uint32_t kps = (uint32_t)a.k_sp, kbs = (uint32_t)a.k_sb;
+  const uint32_t vps = (uint32_t)a.v_sp, vbs = (uint32_t)a.v_sb;
+  const int32_t pmax = (int32_t)min(a.num_pages - 1, (int64_t)INT32_MAX);
+  auto issue_copy8 = [&](uint8_t* kd, uint8_t* vd, int b, const int32_t (&raw)[NI8]) {
+#pragma unroll
+    for (int i = 0; i < NI8; ++i) {
+      const int q0 = (wave * NI8 + i) * 64;   // first staging chunk of this instruction
+      const int j = (q0 + lane) % CPR8;
+      const uint32_t page = (uint32_t)min(max(raw[i], 0), pmax);
+      const uint32_t slot = (uint32_t)(copy_token(b, i) & bmask);
+      const char* gk = kbase + ((uint64_t)page * kps + (slot * kbs + 16u * j));
+      const char* gv = vbase + ((uint64_t)page * vps + (slot * vbs + 16u * j));
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
+                                       (__attribute__((address_space(3))) void*)(&kd[16 * q0]),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gv),
+                                       (__attribute__((address_space(3))) void*)(&vd[16 * q0]),
+                                       16, 0, 0);
+    }
+  };
+  // Widen the copied block (exact e4m3 -> bf16) into the compute layout: chunk c of
+  // token t's K row at slot c ^ kswz(t), of its V row at slot c ^ vswz(t).
+  auto widen = [&](const uint8_t* ks, const uint8_t* vs) {
+#pragma unroll
+    for (int k8 = 0; k8 < KB * CPR8 / 512; ++k8) {
+      const int q = tid + 512 * k8;
+      const int t = q / CPR8, j = q % CPR8;
+      const u32x4 wk = *reinterpret_cast<const u32x4*>(ks + 16 * q);
+      const u32x4 wv = *reinterpret_cast<const u32x4*>(vs + 16 * q);
+      *reinterpret_cast<bf16x8*>(&kb[8 * (t * CPR + ((2 * j) ^ kswz<D>(t)))]) =
+          e4m3x8_to_bf16x8(wk[0], wk[1]);
+      *reinterpret_cast<bf16x8*>(&kb[8 * (t * CPR + ((2 * j + 1) ^ kswz<D>(t)))]) =
+          e4m3x8_to_bf16x8(wk[2], wk[3]);
+      *reinterpret_cast<bf16x8*>(&vb[8 * (t * CPR + ((2 * j) ^ vswz<D>(t)))]) =
+          e4m3x8_to_bf16x8(wv[0], wv[1]);
+      *reinterpret_cast<bf16x8*>(&vb[8 * (t * CPR + ((2 * j + 1) ^ vswz<D>(t)))]) =
+          e4m3x8_to_bf16x8(wv[2], wv[3]);
+    }
+  };
+
+  // V^T operand reads.  The P^T operand of k-step kk holds, in lane half hf, the
+  // probabilities of tokens 16kk + 4hf + 0..3 and 16kk + 8 + 4hf + 0..3 (the order
+  // the S^T accumulator produces them in), so V^T must list the same tokens.  Lane
+  // l of a 16-lane group g = l >> 4 reads 8 bytes of token row 4hf + (l & 15) / 4
+  // (+8 for the second read, +16kk for k-step kk) at column 32dt + 16(g & 1) +
+  // 4(l & 3); the transposing read hands lane l column 32dt + (l & 31) over the
+  // 4 tokens read by its group.
+  const int vr_tok = 4 * hf + ((lane & 15) >> 2);             // token within a 16-token k-step
+  const int vr_sw = vswz<D>(vr_tok);                           // token & 3 is fixed per lane
+  const int vr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-column d-tile
+  auto v_elem = [&](int kk, int dt, int second) -> int {
+    const int tok = 16 * kk + vr_tok + 8 * second;
+    const int col = 32 * dt + vr_col;
+    return tok * D + 8 * ((col >> 3) ^ vr_sw) + (col & 7);
+  };
+
+  // ---- tile pieces.  Tile T of a block is block tokens 32T .. 32T+31; S^T element
+  // i of a lane is token 32T + 8(i/4) + 4hf + i%4.
+  auto read_k = [&](auto& kc, int T, bf16x8 (&kop)[NS]) {
+    const int t = 32 * T + n32;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      kop[s] = *reinterpret_cast<const bf16x8*>(&kc[8 * (t * CPR + ((2 * s + hf) ^ kswz<D>(t)))]);
+  };
+  auto s_mfma = [&](const bf16x8 (&kop)[NS]) -> f32x16 {
+    f32x16 sacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = 0.f;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) sacc = mfma32(kop[s], qop[s], sacc);
+    return sacc;
+  };
+  auto read_v = [&](auto& vc, int kk, bf16x8 (&vop)[NDT]) {   // k-step kk of the block
+    typedef short v4s __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 0)]));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4s*)(&vc[v_elem(kk, dt, 1)]));
+      const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+      vop[dt] = __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+    }
+  };
+  // tile max (base-2 units); the reference max is raised (rescaling O and l) only
+  // when a tile exceeds it by kLazy
+  auto tile_max = [&](const f32x16& sacc) -> float {
+    float mb = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mb = fmaxf(mb, sacc[i]);
+    mb = halves_max(mb) * c;
+    return (mb > m_run + kLazy) ? mb : m_run;
+  };
+  auto raise_max = [&](float m_new) {
+    if (__any(m_new != m_run)) {
+      // alpha = 1 where the reference stays (also rows with no visible key yet:
+      // -inf - -inf would be NaN); a row leaving -inf gets exp2(-inf) = 0
+      const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[dt][i] *= alpha;
+      m_run = m_new;
+    }
+  };
+  // probabilities against the current reference max, packed as the P^T operands
+  // of the tile's two 16-token k-steps; their sum goes into l
+  auto exp_pack = [&](const f32x16& sacc, bf16x8 (&pop)[2]) {
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+    float p[16];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+      psum += p[i];
+    }
+    l_run += psum;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      u32x4 pw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(p[8 * kh + 2 * h], p[8 * kh + 2 * h + 1]);
+      pop[kh] = __builtin_bit_cast(bf16x8, pw);
+    }
+  };
+  auto o_mfma = [&](const bf16x8 (&vop)[NDT], const bf16x8& pop) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(vop[dt], pop, oacc[dt]);
+  };
+
+  auto compute = [&](auto& kc, auto& vc, int tb) {
+    bf16x8 kop[NS];
+    bf16x8 vop[NDT];
+    bf16x8 pop[2];
+    if (tb >= lo_max && tb + KB <= hi_min) {
+      // Fast path (no masks), software-pipelined over the block's tiles: while the
+      // probabilities of tile T are formed, the S^T MFMAs of tile T+1 run and the
+      // K operands of tile T+2 and the V operands of tile T are in flight.
+      read_k(kc, 0, kop);
+      f32x16 sa = s_mfma(kop);
+      if (NT > 1) read_k(kc, 1, kop);
+      raise_max(tile_max(sa));
+#pragma unroll
+      for (int T = 0; T < NT; ++T) {
+        read_v(vc, 2 * T, vop);
+        f32x16 sb;
+        if (T + 1 < NT) {
+          sb = s_mfma(kop);
+          if (T + 2 < NT) read_k(kc, T + 2, kop);
+        }
+        exp_pack(sa, pop);
+        o_mfma(vop, pop[0]);
+        read_v(vc, 2 * T + 1, vop);
+        const float m_next = T + 1 < NT ? tile_max(sb) : 0.f;
+        o_mfma(vop, pop[1]);
+        if (T + 1 < NT) {
+          raise_max(m_next);
+          sa = sb;
+        }
+      }
+    } else {
+      for (int T = 0; T < NT; ++T) {
+        const int tt0 = tb + 32 * T;
+        if ((tt0 >= hi_max) | (tt0 + 32 <= lo_min)) continue;   // no row of the wave sees it
+        read_k(kc, T, kop);
+        f32x16 sacc = s_mfma(kop);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int tk = tt0 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (!((tk >= row_lo) & (tk < row_hi))) sacc[i] = -INFINITY;
+        }
+        raise_max(tile_max(sacc));
+        exp_pack(sacc, pop);
+        read_v(vc, 2 * T, vop);
+        o_mfma(vop, pop[0]);
+        read_v(vc, 2 * T + 1, vop);
+        o_mfma(vop, pop[1]);
+      }
+    }
+  };
+
+  // ---- Q rows.  Each wave copies its 32 rows HBM -> LDS with the load-to-LDS path
+  // (whole rows per instruction, 16 bytes per lane) into the compute tiles, rows
+  // 0-15 into kb and 16-31 into vb, and reads its operands from there before
+  // block 0 is widened over them; chunk c of row r sits at slot c ^ (r mod CPR).  Rows past
+  // the tile's end fetch its last row (never stored).  Loaded by the lane that
+  // owns the row, a load instruction would touch 32 rows 32 bytes at a time.
+  static_assert(16 * 2 * D == NI * 1024, "a wave's Q half-tile fills its copy region");
+  auto issue_q = [&]() {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int o = 1024 * i + 16 * lane;             // byte within the half-tile
+        const int r = o / (2 * D), j = (o % (2 * D)) / 16;
+        const int rl_c = min(wave * 32 + 16 * pt + r, it.nrows - 1);
+        const int rho_c = it.row0 + rl_c;
+        const __bf16* src = static_cast<const __bf16*>(a.q) +
+                            ((int64_t)rq.q_off + (rho_c >> lgG)) * a.q_st +
+                            (int64_t)(it.hk * G + (rho_c & (G - 1))) * a.q_sh +
+                            8 * (j ^ (r & (CPR - 1)));
+        __bf16* dst = (pt ? vb : kb) + 512 * (wave * NI + i);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+      }
+  };
+  auto read_q = [&]() {
+    const int r = n32 & 15;
+    const __bf16* qs = (n32 < 16 ? kb : vb) + 512 * wave * NI + r * D;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qop[s] = *reinterpret_cast<const bf16x8*>(qs + 8 * ((2 * s + hf) ^ (r & (CPR - 1))));
+  };
+
+  // ---- one block: start the copy of block b+1 (page ids loaded during block b-1)
+  // and the page-id loads of block b+2, widen block b, then compute it
+  int32_t raw[NI8];
+  auto step = [&](int b, const uint8_t* kc8, const uint8_t* vc8, uint8_t* kn8, uint8_t* vn8) {
+    if (b + 1 < nb) issue_copy8(kn8, vn8, b + 1, raw);
+    if (b + 2 < nb) load_pages(b + 2, raw);
+    widen(kc8, vc8);
+    __syncthreads();                            // the widened block is complete
+    if (wave_active) compute(kb, vb, it.kv_begin + b * KB);
+    __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
+    __syncthreads();                            // and no wave still reads kb / vb
+  };
+
+  // ---- prologue: block 0 and the Q rows copied, page ids of block 1 loaded (an
+  // empty KV range -- a non-causal request without pages -- has no blocks)
+  if (nb > 0) {
+    load_pages(0, raw);
+    issue_copy8(k8a, v8a, 0, raw);
+  }
+  issue_q();
+  if (nb > 1) load_pages(1, raw);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  read_q();
+  __builtin_amdgcn_s_waitcnt(kLgkmcntZero);
+  __syncthreads();   // every wave holds its Q operands before block 0 is widened over them
+
+  for (int b = 0; b < nb; b += 2) {
+    step(b, k8a, v8a, k8b, v8b);
+    if (b + 1 >= nb) break;
+    step(b + 1, k8b, v8b, k8a, v8a);
+  }
+
+  // ---- finalise: O^T element i of tile dt is column d = 32dt + 8(i/4) + 4hf + i%4
+  const float l_tot = halves_sum(l_run);
+  const bool any = l_tot > 0.f;
+  const float inv = any ? a.v_scale / l_tot : 0.f;
+  const float lse2 = any ? m_run + log2f(l_tot) : -INFINITY;
+  // The row's addressing is recomputed here from a lane id the compiler cannot
+  // see through, so none of it is kept live (and spilled) across the block loop.
+  int le = __lane_id();
+  asm volatile("" : "+v"(le));
+  const int n32e = le & 31, hfe = le >> 5;
+  const int rle = wave * 32 + n32e;
+  const bool rvalide = rle < it.nrows;
+  const int rho = it.row0 + rle;
+  const int64_t qtok = (int64_t)rq.q_off + (rho >> lgG);
+  const int head = it.hk * G + (rho & (G - 1));
+  if (it.pbase < 0) {
+    // Every wave is past the last block's barrier, so all LDS is free: wave w
+    // stages its 32 bf16 rows (padded by 16 bytes against bank conflicts) in its
+    // own slice, then stores whole rows, 16 bytes per lane and CPR lanes per row.
+    // Stored from the lane that owns the row, a store instruction would touch 32
+    // rows 8 bytes at a time.
+    constexpr int RS = 2 * D + 16;              // staged row stride in bytes
+    constexpr int RPI = 64 / CPR;               // rows per store instruction
+    static_assert(32 * RS <= TILE, "a wave's staged rows fit in its LDS slice");
+    static_assert(KB * D == TILE, "an fp8 staging buffer is a wave's slice");
+    char* const st = wave < 4 ? reinterpret_cast<char*>(wave < 2 ? kb : vb) + (wave & 1) * TILE
+                              : reinterpret_cast<char*>(wave == 4 ? k8a : wave == 5 ? k8b : wave == 6 ? v8a : v8b);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hfe;
+        *reinterpret_cast<u32x2*>(st + n32e * RS + 2 * d0) =
+            u32x2{pack_bf16x2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                  pack_bf16x2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv)};
+      }
+    if (rvalide && a.lse && hfe == 0) a.lse[qtok * a.l_st + (int64_t)head * a.l_sh] = lse2 * kLn2;
+    __syncthreads();
+    const int c16 = le % CPR;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = i * RPI + le / CPR;        // row of the wave
+      const u32x4 v = *reinterpret_cast<const u32x4*>(st + rr * RS + 16 * c16);
+      const int rl2 = wave * 32 + rr;
+      if (rl2 < it.nrows) {
+        const int rho2 = it.row0 + rl2;
+        const int head2 = it.hk * G + (rho2 & (G - 1));
+        uint16_t* op = static_cast<uint16_t*>(a.out) + ((int64_t)rq.q_off + (rho2 >> lgG)) * a.o_st +
+                       (int64_t)head2 * a.o_sh;
+        *reinterpret_cast<u32x4*>(op + 8 * c16) = v;
+      }
+    }
+  } else {
+    if (!rvalide) return;
+    const int64_t prow = (int64_t)it.pbase + rle;
+    float* pp = a.part_o + prow * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hfe;
+        *reinterpret_cast<f32x4*>(pp + d0) =
+            f32x4{oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv, oacc[dt][4 * g + 2] * inv,
+                  oacc[dt][4 * g + 3] * inv};
+      }
+    if (hfe == 0) a.part_lse[prow] = lse2;
+  }
+}
+
+
 }  // namespace
 
 hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s) {
@@ -748,9 +844,9 @@ hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype
   } else if (D == 64 && kv_dtype == AK_BF16) {
     hipLaunchKernelGGL((attn_large_dma_kernel<64, kDmaKB>), grid, dim3(512), 0, s, a);
   } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<128, true>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma8_kernel<128, kDmaKB>), grid, dim3(512), 0, s, a);
   } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<64, true>), grid, dim3(512), 0, s, a);
+    hipLaunchKernelGGL((attn_large_dma8_kernel<64, kDmaKB>), grid, dim3(512), 0, s, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -132,6 +132,12 @@ EDGE = [
     ("head_dim_64", [1, 37, 1], [333, 260, 64], 16, 16, 4, 64, "bf16", "bf16", True, (-1, 20)),
     ("non_causal", [64, 200, 1], [64, 511, 90], 16, 8, 2, 128, "bf16", "bf16", False, (-1,)),
     ("fp8_prefill", [1, 150, 2], [3000, 900, 65], 64, 16, 2, 128, "bf16", "fp8", True, (-1, 300)),
+    # fp8 caches on the large-tile path: head_dim 64, token slots (page 1), several
+    # 128-token blocks with a ragged tail, non-causal, and a window straddling blocks
+    ("fp8_prefill_d64", [37, 1, 300], [333, 64, 700], 16, 16, 4, 64, "bf16", "fp8", True, (-1, 20)),
+    ("fp8_prefill_page1", [129, 64, 1], [1000, 64, 300], 1, 32, 8, 128, "bf16", "fp8", True, (-1, 200)),
+    ("fp8_noncausal", [64, 200, 1], [64, 511, 90], 16, 8, 2, 128, "bf16", "fp8", False, (-1,)),
+    ("fp8_window_straddle", [128, 128], [178, 300], 16, 8, 8, 128, "bf16", "fp8", True, (80, 40, 7)),
     ("fp32_prefill", [1, 70, 3], [40, 100, 200], 16, 8, 2, 64, "f32", "f32", True, (-1, 10)),
     ("fp32_d128", [2, 1], [33, 129], 4, 4, 1, 128, "f32", "f32", True, (-1,)),
     ("multi_row_small", [2, 4, 3], [2000, 1500, 999], 16, 8, 2, 128, "bf16", "bf16", True, (-1, 700)),
