@@ -465,24 +465,55 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   if (threadIdx.x == 0)
     __hip_atomic_store(a.counters + it.merge0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!active) return;
+  // The row's 16 lanes read its parts' LSEs 16 at a time and reduce the max in
+  // their group; lane j of the group then holds part (chunk + j)'s weight, which
+  // the weighted sum takes by a lane broadcast, summing the parts in order with
+  // four part rows in flight (the same arithmetic as one part at a time).
   const MergeJob jb = a.merges[it.merge0 + row];
+  const int sub = threadIdx.x & 15;          // lane within the row's group
+  const int grp = threadIdx.x & 48;          // first lane of the group in the wave
+  auto lse_of = [&](int s) {
+    return __hip_atomic_load(a.part_lse + jb.pfirst + (int64_t)s * jb.pstride, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+  };
   float m = -INFINITY;
-  for (int s = 0; s < jb.count; ++s)
-    m = fmaxf(m, __hip_atomic_load(a.part_lse + jb.pfirst + (int64_t)s * jb.pstride, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT));
+  for (int s = sub; s < jb.count; s += 16) m = fmaxf(m, lse_of(s));
+#pragma unroll
+  for (int k = 8; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k, 64));
 #pragma unroll
   for (int cc = 0; cc < CPT; ++cc) o[cc] = 0.f;
   float wsum = 0.f;
   if (m != -INFINITY) {
-    for (int s = 0; s < jb.count; ++s) {
-      const int64_t prow = jb.pfirst + (int64_t)s * jb.pstride;
-      const float w = exp2f(__hip_atomic_load(a.part_lse + prow, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT) - m);   // -inf parts weigh 0
-      const float* po = a.part_o + prow * D + c0;
+    for (int s0 = 0; s0 < jb.count; s0 += 16) {
+      const int n = min(16, jb.count - s0);
+      const float wl = sub < n ? exp2f(lse_of(s0 + sub) - m) : 0.f;   // -inf parts weigh 0
+      auto row_of = [&](int s) { return a.part_o + (jb.pfirst + (int64_t)s * jb.pstride) * D + c0; };
+      int j = 0;
+      for (; j + 4 <= n; j += 4) {
+        float v[4][CPT];
 #pragma unroll
-      for (int cc = 0; cc < CPT; ++cc)
-        o[cc] += w * __hip_atomic_load(po + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wsum += w;
+        for (int u = 0; u < 4; ++u) {
+          const float* po = row_of(s0 + j + u);
+#pragma unroll
+          for (int cc = 0; cc < CPT; ++cc)
+            v[u][cc] = __hip_atomic_load(po + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float w = __shfl(wl, grp + j + u, 64);
+#pragma unroll
+          for (int cc = 0; cc < CPT; ++cc) o[cc] += w * v[u][cc];
+          wsum += w;
+        }
+      }
+      for (; j < n; ++j) {
+        const float w = __shfl(wl, grp + j, 64);
+        const float* po = row_of(s0 + j);
+#pragma unroll
+        for (int cc = 0; cc < CPT; ++cc)
+          o[cc] += w * __hip_atomic_load(po + cc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        wsum += w;
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
