@@ -22,8 +22,9 @@ batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
 the mixed chunked-prefill + decode step with full and sliding-window layers
 ("mixed"), the fp8 long-context decode ("longfp8"), decode requests sharing
 a 4096-token prefix run plainly (with the shared-pages flag, and streamed) and
-as a cascade ("cascade"), and a small
-decode batch issued eagerly and as a replayed graph over a fixed plan ("graph").
+as a cascade ("cascade"), and decode issued eagerly and as a replayed graph
+over a fixed plan, on a small batch ("graph") and on the 64-request batch
+above ("graph64").
 Two optional legs measure the large-tile kernel alone: on long uniform prompts
 ("prefill_shapes") and the fixed and per-block cost of a 256-row segment
 ("segcost").
@@ -409,11 +410,14 @@ def measure_cascade(ak, torch, dev, wl, n_layers, steps, warmup):
     return res
 
 
-def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup):
-    """Small-batch decode, where launch cost dominates: the same step (plan, then
-    store_kv + run per layer) issued eagerly, and as a fixed plan updated on the
-    host plus one replay of a graph holding every layer's store and run.  Wall
-    time per step (host and device), the step's outputs compared bit for bit."""
+def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup, merge_in_kernel=True):
+    """The same decode step (plan, then store_kv + run per layer) issued eagerly,
+    and as a fixed plan updated on the host plus one replay of a graph holding
+    every layer's store and run.  Wall time per step (host and device), the
+    step's outputs compared bit for bit.  On a small batch launch cost dominates
+    (there the parts of a split merge inside the attention kernel); on the
+    64-request batch it shows what the gaps between launches cost (there the
+    merge is its own launch, the faster choice at that size, as in the eager step)."""
     log(f"[bench] {wl.name}: R={wl.batch_size} KV tokens={int(wl.kv_lens.sum())} "
         f"layers={n_layers} (eager vs graph replay)")
     layers = make_layers(wl, n_layers, dev)
@@ -422,13 +426,14 @@ def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup):
     hq, hkv, D, B = wl.num_qo_heads, wl.num_kv_heads, wl.head_dim, wl.page_size
 
     def eager_step():
-        plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B)
+        plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, hq, hkv, D, B,
+                          merge_in_kernel=merge_in_kernel)
         for L in layers:
             ak.ak_store_kv(L["kn"], L["vn"], slots, L["kc"], L["vc"])
             ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"])
 
     fixed = ak.ak_plan_fixed(wl.batch_size, wl.total_q, idx, hq, hkv, D, B,
-                             max_query_len=int(wl.q_lens.max()), merge_in_kernel=True)
+                             max_query_len=int(wl.q_lens.max()), merge_in_kernel=merge_in_kernel)
     ak.ak_plan_update(fixed, wl.qo_indptr, wl.kv_indptr, wl.last_page_len)
 
     def body():
@@ -468,8 +473,8 @@ def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup):
            "kv_tokens": int(wl.kv_lens.sum()), "eager_us_per_step": round(eager_us, 1),
            "graph_us_per_step": round(graph_us, 1), "speedup": round(eager_us / graph_us, 2),
            "graph_step_GBs": round(step_bytes / (graph_us * 1e-6) / 1e9, 1),
-           "outputs_identical": bool(same), "capacity": {k: v for k, v in fixed.info().items()
-                                                         if k.startswith("cap_")}}
+           "merge_in_kernel": merge_in_kernel, "outputs_identical": bool(same),
+           "capacity": {k: v for k, v in fixed.info().items() if k.startswith("cap_")}}
     log(f"[bench] {wl.name}: eager {eager_us:.1f} us/step, graph {graph_us:.1f} us/step "
         f"(x{res['speedup']}, {res['graph_step_GBs']} GB/s step-level), identical={same}")
     del layers, g
@@ -555,6 +560,7 @@ WORKLOADS = {
     "longfp8": (lambda W: W.config(5), 4),
     "cascade": (lambda W: W.shared_prefix_decode(), 8),
     "graph": (lambda W: W.small_batch_decode(), 32),
+    "graph64": (lambda W: W.config(2), 32),
     "prefill_shapes": (None, 2),
     "segcost": (None, 2),
 }
@@ -566,9 +572,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
-    ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph",
-                    help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph "
-                         "(default), prefill_shapes, segcost ('' for none)")
+    ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph,graph64",
+                    help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph,"
+                         "graph64 (default), prefill_shapes, segcost ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy timed as bandwidth context (0: skip)")
@@ -592,8 +598,9 @@ def main():
         if name == "cascade":
             extra[name] = measure_cascade(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
             continue
-        if name == "graph":
-            extra[name] = measure_graph(ak, torch, dev, fac(W), nl, max(5, args.steps), 3)
+        if name in ("graph", "graph64"):
+            extra[name] = measure_graph(ak, torch, dev, fac(W), nl, max(5, args.steps), 3,
+                                        merge_in_kernel=name == "graph")
             continue
         if name == "prefill_shapes":
             extra[name] = measure_prefill_shapes(ak, torch, dev)
@@ -645,7 +652,7 @@ def main():
         "tokens_per_s_per_layer": round(dec["tok_s_layer"], 1),
     }
     for name, r in extra.items():
-        if name in ("cascade", "graph", "prefill_shapes", "segcost"):
+        if name in ("cascade", "graph", "graph64", "prefill_shapes", "segcost"):
             line[name] = r
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
