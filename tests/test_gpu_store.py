@@ -168,3 +168,52 @@ def test_fp8_widening_exhaustive():
     got_bits = got.cpu().view(torch.int16).numpy().view(np.uint16)
     exp_bits = C.bf16_encode(C.e4m3_decode(codes).astype(np.float32))
     assert np.array_equal(got_bits, exp_bits)
+
+
+def _draw_store(seed: int):
+    """A seeded store: token count (0 to 5000, one empty store, one case past the
+    launch's 8192-block cap so the grid-stride loop runs), heads, head size, page size,
+    dtype pair, per-tensor scale, value magnitudes from 2^-20 to 600 (fp8
+    saturation and subnormals included) and 0-20% padding slots."""
+    rng = np.random.default_rng(4200 + seed)
+    N = 40000 if seed == 0 else int(rng.integers(0, 5001))
+    if seed == 11:
+        N = 0
+    H = int(rng.choice([1, 3, 8]))
+    D = int(rng.choice([8, 64, 128, 256]))
+    if seed == 0:
+        H, D = 1, 64
+    B = int(rng.choice([1, 16, 64]))
+    P = (N + B - 1) // B + int(rng.integers(1, 9))
+    src, dst = [("f32", "f32"), ("f32", "bf16"), ("f32", "fp8"), ("bf16", "bf16"),
+                ("bf16", "fp8")][int(rng.integers(5))]
+    scale = float(2.0 ** rng.uniform(-5, 2)) if dst == "fp8" else 1.0
+    mag = 2.0 ** rng.uniform(-20, np.log2(600), size=(N, H, 1))
+    vals = (rng.standard_normal((N, H, D)) * mag).astype(np.float32)
+    slots = rng.permutation(P * B)[:N].astype(np.int64)
+    slots[rng.random(N) < rng.uniform(0, 0.2)] = -1
+    return N, H, D, P, B, src, dst, scale, vals, slots
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_store_random_shapes_bit_exact(seed):
+    N, H, D, P, B, src, dst, scale, vals, slots = _draw_store(seed)
+    say(f"[store] random {seed}: N={N} H={H} D={D} P={P} B={B} {src}->{dst} scale={scale:.4g}")
+    if src == "bf16":
+        vals = C.bf16_decode(C.bf16_encode(vals)).astype(np.float32)
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    if src == "f32":
+        k = torch.from_numpy(vals).cuda()
+    else:
+        k = torch.from_numpy(C.bf16_encode(vals).view(np.int16)).view(torch.bfloat16).cuda()
+    v = -k
+    kc = torch.zeros(P, B, H, D, dtype=tdt[dst], device="cuda")
+    vc = torch.zeros_like(kc)
+    ak.ak_store_kv(k, v, torch.from_numpy(slots).cuda(), kc, vc, scale, scale)
+    torch.cuda.synchronize()
+    zero = np.zeros((P, B, H, D), dtype=np.float32)
+    for sign, cache in ((1, kc), (-1, vc)):
+        oc = A.Cache(A.encode(zero, dst, scale), dst, scale)
+        A.store_kv(oc, sign * vals, slots)
+        got = _bits(cache).reshape(-1)
+        assert np.array_equal(got.view(np.uint8), oc.codes.reshape(-1).view(np.uint8))
