@@ -37,6 +37,24 @@ BATCHES = [
 ]
 
 
+def _random_batch(seed):
+    """A seeded batch within the captured capacities: 1 to 48 requests, mostly
+    decodes, some 2-5 token queries and 6-64 token extend chunks, KV lengths up
+    to a table row's 200 pages."""
+    rng = np.random.default_rng(seed)
+    q = []
+    for _ in range(int(rng.integers(1, R_MAX + 1))):
+        u = rng.random()
+        q.append(1 if u < 0.75 else int(rng.integers(2, 6)) if u < 0.9 else int(rng.integers(6, 65)))
+    while sum(q) > T_MAX:
+        q[int(np.argmax(q))] //= 2
+    kv = [int(rng.integers(qi, ROW_PAGES * B + 1)) for qi in q]
+    return (seed, q, kv)
+
+
+BATCHES += [_random_batch(s) for s in (36, 37, 38)]
+
+
 def _workload(seed, q_lens, kv_lens):
     return W.custom(seed=seed, q_lens=q_lens, kv_lens=kv_lens, page_size=B, num_qo_heads=HQ,
                     num_kv_heads=HKV, head_dim=D, name=f"graph_{seed}")
