@@ -55,33 +55,65 @@ def test_long_decode_fp8_reduced():
 
 # ---------------------------------------------- full sizes, sampled checks
 
-def _sample_rows(wl, r, k=24):
+def _sample_rows(wl, r, k=24, window=-1):
+    """Query rows of request r to compare: all of a short request; otherwise the
+    first and last rows, the middle, k random rows, rows either side of every
+    64-token boundary (a 256-row large tile holds 64 query tokens at group 4)
+    and, with a window, rows whose window start crosses a 128-token KV block."""
     n = int(wl.q_lens[r])
     if n <= k:
         return np.arange(n)
     rng = np.random.default_rng(r)
     pick = set([0, 1, n // 2, n - 2, n - 1]) | set(rng.choice(n, size=k, replace=False).tolist())
-    return np.asarray(sorted(pick))
+    for b in range(64, n, 64 * max(1, n // 1024)):
+        pick |= {b - 1, b}
+    if window >= 0:
+        L = int(wl.kv_lens[r])
+        start = L - n + np.arange(n) - window          # first visible key of each row
+        cross = np.nonzero((start > 0) & (start % 128 == 0))[0]
+        for j in cross[:: max(1, len(cross) // 8)]:
+            pick |= {int(j) - 1, int(j), int(j) + 1}
+    return np.asarray(sorted(x for x in pick if 0 <= x < n))
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5])
-def test_full_size_sampled(k):
-    wl = W.config(k)
-    say(f"[parity-full] config {k}: R={wl.batch_size} tokens={wl.total_q} "
+def _full_size_requests(wl, k):
+    """Requests compared at full size: the longest, the shortest, a few random
+    ones and every request with more than one query row."""
+    order = np.argsort(-wl.kv_lens)
+    if k == 5:
+        reqs = {int(order[0]), int(order[-1])}
+    else:
+        rng = np.random.default_rng(k)
+        reqs = set(order[:3].tolist()) | set(order[-2:].tolist()) | \
+            set(rng.choice(wl.batch_size, size=min(6, wl.batch_size), replace=False).tolist())
+    reqs |= set(np.nonzero(wl.q_lens > 1)[0].tolist())
+    return sorted(int(r) for r in reqs)
+
+
+def _check_full_size(wl, k):
+    say(f"[parity-full] {wl.name} (config {k}): R={wl.batch_size} tokens={wl.total_q} "
         f"kv={int(wl.kv_lens.sum())}")
     d = prepare(wl)
-    order = np.argsort(-wl.kv_lens)
-    rng = np.random.default_rng(k)
-    if k == 5:
-        reqs = [int(order[0]), int(order[-1])]
-    else:
-        reqs = sorted(set(order[:3].tolist()) | set(order[-2:].tolist()) |
-                      set(rng.choice(wl.batch_size, size=min(6, wl.batch_size), replace=False).tolist()))
+    reqs = _full_size_requests(wl, k)
+    say(f"  compared requests {reqs}")
     for window in wl.windows:
         plan = plan_for(wl, d, window)
         say(f"  plan {ak.ak_plan_info(plan)}")
         out, lse = run(wl, d, plan)
-        check(wl, out, lse, window, requests=reqs, rows_of=lambda r: _sample_rows(wl, r))
+        check(wl, out, lse, window, requests=reqs,
+              rows_of=lambda r, w=window: _sample_rows(wl, r, window=w))
+    del d
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_full_size_sampled(k):
+    _check_full_size(W.config(k), k)
+
+
+def test_full_size_sampled_mixed_shuffled():
+    # the mixed step with its requests in a random order (the chunk is not first)
+    _check_full_size(W.config(4, shuffle=True), 4)
 
 
 # ------------------------------------------------------------- properties
