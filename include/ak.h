@@ -283,6 +283,32 @@ void ak_plan_destroy(ak_plan_t* plan);
 ak_status ak_run(const ak_plan_t* plan, const ak_tensor* q, const ak_tensor* k_cache,
                  const ak_tensor* v_cache, ak_tensor* out, ak_tensor* lse, void* stream);
 
+/* ak_run_noalloc -- plan and run one layer in a single call that allocates
+ * nothing, for callers that cannot allocate: code under stream capture, tight
+ * serving loops, harnesses that forbid hipMalloc.
+ *
+ * Computes exactly what ak_plan followed by ak_run computes with the same
+ * arguments (same work list, same kernels, bitwise the same out and lse); the
+ * arguments mean what they mean there, `opts->stream` is ignored and `stream`
+ * carries both the metadata upload and the kernels.  Instead of a plan
+ * workspace, the work list, merge list, arrival counters and split partials
+ * live in one fixed device array of 64 MiB that the library holds on every
+ * device it runs on until the process ends; a batch whose work list and split
+ * partials need more returns AK_ERR_UNSUPPORTED before anything is enqueued
+ * (use ak_plan + ak_run for it).  No device or pinned memory is allocated and
+ * nothing is freed; the work list is copied from pageable host memory, which
+ * may wait for earlier work on `stream`.  Every call on one device shares that
+ * array: calls that overlap in time on one device (different streams, or
+ * several host threads) race and must be serialised by the caller; calls on one
+ * stream are ordered.  Errors: those of ak_plan and ak_run, and AK_ERR_HIP if
+ * the array's device address cannot be obtained. */
+ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                         const int32_t* kv_indices, const int32_t* last_page_len,
+                         int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t page_size, int32_t causal, int32_t window,
+                         const ak_plan_opts* opts, const ak_tensor* q, const ak_tensor* k_cache,
+                         const ak_tensor* v_cache, ak_tensor* out, ak_tensor* lse, void* stream);
+
 /* ----------------------------------------------------------- diagnostics */
 
 /* Thread-local text of the last error (empty string if none).  Owned by the

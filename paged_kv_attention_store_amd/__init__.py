@@ -12,6 +12,8 @@ Entry points (same names as the C ABI):
             num_kv_heads, head_dim, page_size, causal=True, window=-1, ...) -> Plan
     ak_run(plan, q, k_cache, v_cache, out=None, lse=None, k_scale=1.0, v_scale=1.0)
     ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None)
+    ak_run_noalloc(qo_indptr, kv_indptr, kv_indices, last_page_len, ..., q, k_cache,
+                   v_cache, out, lse)   (plan + run without allocating)
     ak_plan_destroy, ak_plan_info, ak_plan_export, ak_gather_slots,
     ak_profile_enable, ak_profile_read, ak_last_error, ak_version
 """
@@ -49,7 +51,7 @@ EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_erro
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
             "ak_merge_states", "ak_csr_from_block_table", "ak_slot_mapping", "ak_plan_fixed",
             "ak_plan_update",
-            "ak_profile_read", "ak_version", "ak_fp8_to_bf16"]
+            "ak_profile_read", "ak_version", "ak_fp8_to_bf16", "ak_run_noalloc"]
 
 
 class AkError(RuntimeError):
@@ -98,6 +100,9 @@ def _load():
     lib.ak_plan_destroy.restype = None
     lib.ak_run.argtypes = [ctypes.c_void_p] + [P(AkTensor)] * 5 + [ctypes.c_void_p]
     lib.ak_run.restype = ctypes.c_int
+    lib.ak_run_noalloc.argtypes = [i32p, i32p, ctypes.c_void_p, i32p] + [ctypes.c_int32] * 7 + [
+        P(AkPlanOpts)] + [P(AkTensor)] * 5 + [ctypes.c_void_p]
+    lib.ak_run_noalloc.restype = ctypes.c_int
     lib.ak_last_error.argtypes = []
     lib.ak_last_error.restype = ctypes.c_char_p
     lib.ak_plan_info.argtypes = [ctypes.c_void_p, P(ctypes.c_int64), ctypes.c_int32]
@@ -345,6 +350,44 @@ def ak_run(plan: Plan, q, k_cache, v_cache, out=None, lse=None, k_scale: float =
     _check(_lib.ak_run(plan.handle, ctypes.byref(dq), ctypes.byref(dk), ctypes.byref(dv),
                        ctypes.byref(do), ctypes.byref(dl) if dl is not None else None,
                        _stream_ptr(stream)))
+    return out, lse
+
+
+def ak_run_noalloc(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int,
+                   num_kv_heads: int, head_dim: int, page_size: int, q, k_cache, v_cache, out, lse=None,
+                   causal: bool = True, window: int = -1, k_scale: float = 1.0, v_scale: float = 1.0,
+                   sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
+                   min_chunk: int = 0, merge_in_kernel: bool = False, shared_pages: bool = False,
+                   stream=None):
+    """Plan and run one layer without any allocation by the library (its split
+    workspace is a fixed device array); out (and lse) must be given."""
+    qo, qo_p = _host_i32(qo_indptr)
+    kv, kv_p = _host_i32(kv_indptr)
+    last, last_p = _host_i32(last_page_len)
+    R = len(qo) - 1
+    if len(kv) != R + 1 or len(last) != R:
+        raise ValueError("qo_indptr/kv_indptr need batch_size+1 entries, last_page_len batch_size")
+    opts = AkPlanOpts()
+    opts.sm_scale = float(sm_scale) if sm_scale else 0.0
+    opts.num_cus = int(num_cus)
+    opts.max_splits = int(max_splits)
+    opts.min_chunk = int(min_chunk)
+    opts.flags = ((AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
+    idx_ptr = None
+    if kv_indices is not None and kv_indices.numel():
+        import torch
+
+        if kv_indices.dtype != torch.int32 or not kv_indices.is_contiguous():
+            raise TypeError("kv_indices must be a contiguous int32 device tensor")
+        idx_ptr = ctypes.c_void_p(kv_indices.data_ptr())
+    dq, dk, dv, do = (_desc(q), _desc(k_cache, k_scale), _desc(v_cache, v_scale), _desc(out))
+    dl = _desc(lse) if lse is not None else None
+    _check(_lib.ak_run_noalloc(qo_p, kv_p, idx_ptr, last_p, R, num_qo_heads, num_kv_heads,
+                               head_dim, page_size, int(bool(causal)), int(window),
+                               ctypes.byref(opts), ctypes.byref(dq), ctypes.byref(dk),
+                               ctypes.byref(dv), ctypes.byref(do),
+                               ctypes.byref(dl) if dl is not None else None, _stream_ptr(stream)))
     return out, lse
 
 

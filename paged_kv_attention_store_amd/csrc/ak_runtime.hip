@@ -914,6 +914,135 @@ extern "C" ak_status ak_merge_states(const ak_tensor* o_a, const ak_tensor* lse_
   return AK_OK;
 }
 
+// ------------------------------------------------- allocation-free variant
+
+// The device memory behind ak_run_noalloc: one plan's work list, merge list,
+// arrival counters and split partials, in a fixed array each device holds for
+// the life of the process.  Host code never passes `scratch` itself to a kernel
+// or a copy (in host code the name is only a stand-in); it uses the address
+// hipGetSymbolAddress returns on each device.
+namespace ak {
+constexpr size_t kScratchBytes = size_t(64) << 20;
+}
+static __device__ __align__(256) unsigned char scratch[ak::kScratchBytes];
+
+namespace ak {
+namespace {
+
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on `dev` (the current device), looked up
+// once per device.
+ak_status scratch_address(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(AK_ERR_UNSUPPORTED, "ak_run_noalloc: device index out of range");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "ak_run_noalloc: hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(AK_ERR_HIP, "ak_run_noalloc: no device address for the scratch array");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return AK_OK;
+}
+
+thread_local std::vector<unsigned char> t_staging;   // host copy of the uploaded metadata
+
+}  // namespace
+}  // namespace ak
+
+extern "C" ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                    const int32_t* kv_indices, const int32_t* last_page_len,
+                                    int32_t batch_size, int32_t num_qo_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, int32_t page_size, int32_t causal,
+                                    int32_t window, const ak_plan_opts* opts, const ak_tensor* q,
+                                    const ak_tensor* k_cache, const ak_tensor* v_cache,
+                                    ak_tensor* out, ak_tensor* lse, void* stream) {
+  if (opts && (opts->flags & AK_PLAN_HOST_ONLY))
+    return fail(AK_ERR_INVALID_ARG, "ak_run_noalloc: a host-only plan cannot run");
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "ak_run_noalloc: hipGetDevice");
+  unsigned char* base = nullptr;
+  ak_status st = scratch_address(dev, &base);
+  if (st != AK_OK) return st;
+  auto* p = new_plan();
+  if (!p) return fail(AK_ERR_OOM, "ak_run_noalloc: out of host memory");
+  const int cus = opts && opts->num_cus > 0 ? opts->num_cus : device_cus(dev);
+  try {
+    st = build_plan_host(qo_indptr, kv_indptr, last_page_len, batch_size, num_qo_heads,
+                         num_kv_heads, head_dim, page_size, causal, window, opts, cus, p);
+  } catch (const std::bad_alloc&) {
+    st = fail(AK_ERR_OOM, "ak_run_noalloc: out of host memory");
+  }
+  if (st == AK_OK && p->num_kv_pages > 0 && !kv_indices)
+    st = fail(AK_ERR_INVALID_ARG, "ak_run_noalloc: null kv_indices with a non-empty page table");
+  // the same regions as ak_plan's workspace, laid out from the start of scratch
+  const size_t b_req = align256(p->reqs.size() * sizeof(Req));
+  const size_t b_small = align256(p->small_items.size() * sizeof(Item));
+  const size_t b_large = align256(p->large_items.size() * sizeof(Item));
+  const size_t b_merge = align256(p->merges.size() * sizeof(MergeJob));
+  const size_t b_cnt = align256((size_t)p->small_merges * sizeof(int32_t));
+  const size_t b_po = align256((size_t)p->partial_rows * p->D * sizeof(float));
+  const size_t b_pl = align256((size_t)p->partial_rows * sizeof(float));
+  const size_t meta = b_req + b_small + b_large + b_merge + b_cnt;
+  if (st == AK_OK && meta + b_po + b_pl > kScratchBytes) {
+    std::ostringstream os;
+    os << "ak_run_noalloc: the batch's work list and split partials need " << meta + b_po + b_pl
+       << " bytes, more than the " << kScratchBytes << "-byte scratch array (use ak_plan + ak_run)";
+    st = fail(AK_ERR_UNSUPPORTED, os.str());
+  }
+  if (st != AK_OK) {
+    recycle_plan(p);
+    return st;
+  }
+  p->device = dev;
+  p->kv_indices = kv_indices;
+  p->d_buf = base;
+  p->d_bytes = meta + b_po + b_pl;
+  p->d_reqs = reinterpret_cast<Req*>(base);
+  p->d_small = reinterpret_cast<Item*>(base + b_req);
+  p->d_large = reinterpret_cast<Item*>(base + b_req + b_small);
+  p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
+  p->d_merges_large = p->d_merges + p->small_merges;
+  p->d_counters = reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge);
+  p->d_part_o = reinterpret_cast<float*>(base + meta);
+  p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (meta > 0 && p->T > 0) {
+    // one copy of the metadata, arrival counters as zeros (whatever the last
+    // call on this device left in the array)
+    std::vector<unsigned char>& h = t_staging;
+    try {
+      if (h.size() < meta) h.resize(meta);
+    } catch (const std::bad_alloc&) {
+      recycle_plan(p);
+      return fail(AK_ERR_OOM, "ak_run_noalloc: out of host memory");
+    }
+    unsigned char* hp = h.data();
+    std::memset(hp, 0, meta);
+    if (!p->reqs.empty()) std::memcpy(hp, p->reqs.data(), p->reqs.size() * sizeof(Req));
+    if (!p->small_items.empty())
+      std::memcpy(hp + b_req, p->small_items.data(), p->small_items.size() * sizeof(Item));
+    if (!p->large_items.empty())
+      std::memcpy(hp + b_req + b_small, p->large_items.data(), p->large_items.size() * sizeof(Item));
+    if (!p->merges.empty())
+      std::memcpy(hp + b_req + b_small + b_large, p->merges.data(), p->merges.size() * sizeof(MergeJob));
+    // from pageable memory: the host buffer is free for reuse once the call returns
+    e = hipMemcpyAsync(base, hp, meta, hipMemcpyHostToDevice, s);
+    if (e != hipSuccess) {
+      recycle_plan(p);
+      return hip_fail(e, "ak_run_noalloc: metadata upload");
+    }
+  }
+  st = ak_run(p, q, k_cache, v_cache, out, lse, stream);
+  recycle_plan(p);
+  return st;
+}
+
 // ------------------------------------------------------------- diagnostics
 
 extern "C" const char* ak_last_error(void) { return g_err.c_str(); }
