@@ -414,12 +414,20 @@ ak_status ak_plan_export(const ak_plan_t* plan, int32_t* items, int64_t capacity
                          int32_t* kv_lens);
 
 /* ak_gather_slots -- the plan's KV indexing, materialised (debug).
- * For every request r and position t < L_r writes the flat cache slot the
- * attention kernels read, kv_indices[kv_indptr[r] + t / B] * B + t % B, into
- * slots[kv_offset_r + t], where kv_offset_r = sum of L over earlier requests.
- * `slots` is a device int64 array of at least sum_r L_r entries.  Uses the same
- * device-side address arithmetic as ak_run.  Errors: AK_ERR_INVALID_ARG, AK_ERR_HIP. */
-ak_status ak_gather_slots(const ak_plan_t* plan, int64_t* slots, void* stream);
+ * For every request r and position t < L_r writes the flat cache slot
+ * kv_indices[kv_indptr[r] + t / B] * B + t % B ("vLLM attention backend", the
+ * worked example's slot formula) into slots[kv_offset_r + t], where kv_offset_r =
+ * sum of L over earlier requests.  The slot is computed by the device functions
+ * the attention kernels address their K/V rows with -- the page-id read and
+ * clamp, then the row offset -- run with a page stride of B and a slot stride of
+ * 1 instead of the cache's byte strides: `addressing` 0 selects the decode and
+ * fp32 kernels' form (page id clamped as staged, 64-bit row offset), 1 the
+ * prefill kernels' load-to-LDS copy form (raw page id clamped at the copy,
+ * in-page offset in 32 bits).  `slots` is a device int64 array of at least
+ * sum_r L_r entries; the call synchronises the stream.  Errors:
+ * AK_ERR_INVALID_ARG (null argument, host-only plan, addressing not 0 or 1),
+ * AK_ERR_HIP. */
+ak_status ak_gather_slots(const ak_plan_t* plan, int32_t addressing, int64_t* slots, void* stream);
 
 /* ak_fp8_to_bf16 -- the cache's FP8 E4M3 decode, materialised (diagnostics).
  * Widens n E4M3 codes (device uint8 array, n a multiple of 8) into bf16 bit

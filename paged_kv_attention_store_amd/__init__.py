@@ -117,7 +117,7 @@ def _load():
     lib.ak_csr_from_block_table.restype = ctypes.c_int
     lib.ak_slot_mapping.argtypes = [vp, i64, vp, vp, ctypes.c_int32, ctypes.c_int32, vp, i64, vp]
     lib.ak_slot_mapping.restype = ctypes.c_int
-    lib.ak_gather_slots.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.ak_gather_slots.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     lib.ak_gather_slots.restype = ctypes.c_int
     lib.ak_profile_enable.argtypes = [ctypes.c_int32]
     lib.ak_profile_enable.restype = ctypes.c_int
@@ -431,9 +431,11 @@ def ak_plan_export(plan: Plan):
     return items[:n], lens[:info["batch_size"]]
 
 
-def ak_gather_slots(plan: Plan, slots, stream=None) -> None:
-    """Write every request's KV slots (device int64 tensor of sum L entries)."""
-    _check(_lib.ak_gather_slots(plan.handle, ctypes.c_void_p(slots.data_ptr()), _stream_ptr(stream)))
+def ak_gather_slots(plan: Plan, slots, addressing: int = 0, stream=None) -> None:
+    """Write every request's KV slots (device int64 tensor of sum L entries) through
+    the decode kernels' (addressing 0) or the prefill kernels' (1) row addressing."""
+    _check(_lib.ak_gather_slots(plan.handle, int(addressing), ctypes.c_void_p(slots.data_ptr()),
+                                _stream_ptr(stream)))
 
 
 def _dev_i32_matrix(t, name):

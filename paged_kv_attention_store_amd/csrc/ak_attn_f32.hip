@@ -29,7 +29,6 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
   const int G = a.G;
   const float* kc = static_cast<const float*>(a.k_cache) + (int64_t)it.hk * a.k_sh;
   const float* vc = static_cast<const float*>(a.v_cache) + (int64_t)it.hk * a.v_sh;
-  const int32_t bmask = (1 << a.log2B) - 1;
 
   for (int rl = wave; rl < it.nrows; rl += 4) {
     const int rho = it.row0 + rl;
@@ -52,9 +51,8 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
       const int t = tb + lane;
       const bool vis = t < hi;
       const int tc = vis ? t : hi - 1;
-      const int64_t page = kv_page(a.kv_indices, rq.page_off, tc, a.log2B, a.num_pages);
-      const int64_t slot = tc & bmask;
-      const float* kr = kc + page * a.k_sp + slot * a.k_sb;
+      const int32_t page = kv_page_id(a.kv_indices, rq.page_off, tc, a.log2B, a.num_pages);
+      const float* kr = kc + kv_row_offset(page, tc, a.log2B, a.k_sp, a.k_sb);
       float s = 0.f;
 #pragma unroll 8
       for (int d = 0; d < D; d += 4) {
@@ -80,7 +78,7 @@ __global__ __launch_bounds__(256) void attn_f32_kernel(AttnArgs a) {
 #pragma unroll
       for (int i = 0; i < PER; ++i) o[i] *= alpha;
       const int nt = min(64, hi - tb);
-      const int64_t voff = page * a.v_sp + slot * a.v_sb;
+      const int64_t voff = kv_row_offset(page, tc, a.log2B, a.v_sp, a.v_sb);
       for (int k = 0; k < nt; ++k) {
         const float pk = __shfl(p, k, 64);
         const int64_t vo = __shfl(voff, k, 64);

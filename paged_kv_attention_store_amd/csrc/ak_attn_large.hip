@@ -119,7 +119,6 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
 
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * 2;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * 2;
-  const int32_t bmask = (1 << a.log2B) - 1;
   const int nb = (it.kv_end - it.kv_begin + KB - 1) / KB;
 
   // The copy of a block is NI load-to-LDS instructions per wave for K and NI for V;
@@ -132,21 +131,21 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma_kernel(AttnArgs a) {
   };
   auto load_pages = [&](int b, int32_t (&raw)[NI]) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) raw[i] = a.kv_indices[rq.page_off + (copy_token(b, i) >> a.log2B)];
+    for (int i = 0; i < NI; ++i)
+      raw[i] = a.kv_indices[kv_page_index(rq.page_off, copy_token(b, i), a.log2B)];
   };
   const uint32_t kps = (uint32_t)(a.k_sp * 2), kbs = (uint32_t)(a.k_sb * 2);
   const uint32_t vps = (uint32_t)(a.v_sp * 2), vbs = (uint32_t)(a.v_sb * 2);
-  const int32_t pmax = (int32_t)min(a.num_pages - 1, (int64_t)INT32_MAX);
   auto issue_copy = [&](auto& kd, auto& vd, int b, const int32_t (&raw)[NI]) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
       const int q = q0 + lane;
       const int t = q / CPR, j = q % CPR;
-      const uint32_t page = (uint32_t)min(max(raw[i], 0), pmax);
-      const uint32_t slot = (uint32_t)(copy_token(b, i) & bmask);
-      const char* gk = kbase + ((uint64_t)page * kps + (slot * kbs + 16u * (j ^ kswz<D>(t))));
-      const char* gv = vbase + ((uint64_t)page * vps + (slot * vbs + 16u * (j ^ vswz<D>(t))));
+      const uint32_t page = (uint32_t)clamp_page(raw[i], a.num_pages);
+      const int tok = copy_token(b, i);
+      const char* gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, 16u * (j ^ kswz<D>(t)));
+      const char* gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, 16u * (j ^ vswz<D>(t)));
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                        (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
                                        16, 0, 0);
@@ -501,7 +500,6 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma8_kernel(AttnArgs a) {
 
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh;
-  const int32_t bmask = (1 << a.log2B) - 1;
   const int nb = (it.kv_end - it.kv_begin + KB - 1) / KB;
 
   // The fp8 copy of a block is NI8 load-to-LDS instructions per wave for K and NI8
@@ -513,20 +511,20 @@ __global__ __launch_bounds__(512, 2) void attn_large_dma8_kernel(AttnArgs a) {
   };
   auto load_pages = [&](int b, int32_t (&raw)[NI8]) {
 #pragma unroll
-    for (int i = 0; i < NI8; ++i) raw[i] = a.kv_indices[rq.page_off + (copy_token(b, i) >> a.log2B)];
+    for (int i = 0; i < NI8; ++i)
+      raw[i] = a.kv_indices[kv_page_index(rq.page_off, copy_token(b, i), a.log2B)];
   };
   const uint32_t kps = (uint32_t)a.k_sp, kbs = (uint32_t)a.k_sb;
   const uint32_t vps = (uint32_t)a.v_sp, vbs = (uint32_t)a.v_sb;
-  const int32_t pmax = (int32_t)min(a.num_pages - 1, (int64_t)INT32_MAX);
   auto issue_copy8 = [&](uint8_t* kd, uint8_t* vd, int b, const int32_t (&raw)[NI8]) {
 #pragma unroll
     for (int i = 0; i < NI8; ++i) {
       const int q0 = (wave * NI8 + i) * 64;   // first staging chunk of this instruction
       const int j = (q0 + lane) % CPR8;
-      const uint32_t page = (uint32_t)min(max(raw[i], 0), pmax);
-      const uint32_t slot = (uint32_t)(copy_token(b, i) & bmask);
-      const char* gk = kbase + ((uint64_t)page * kps + (slot * kbs + 16u * j));
-      const char* gv = vbase + ((uint64_t)page * vps + (slot * vbs + 16u * j));
+      const uint32_t page = (uint32_t)clamp_page(raw[i], a.num_pages);
+      const int tok = copy_token(b, i);
+      const char* gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, 16u * j);
+      const char* gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, 16u * j);
       __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                        (__attribute__((address_space(3))) void*)(&kd[16 * q0]),
                                        16, 0, 0);

@@ -129,10 +129,9 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   const int first_page = kv_begin >> a.log2B;
   {
     const int npages = ((kv_end - 1) >> a.log2B) - first_page + 1;   // <= kSmallMaxPages (plan)
-    for (int i = threadIdx.x; i < npages; i += 256) {
-      int64_t pg = a.kv_indices[rq.page_off + first_page + i];
-      s_pages[i] = (int32_t)(pg < 0 ? 0 : (pg >= a.num_pages ? a.num_pages - 1 : pg));
-    }
+    for (int i = threadIdx.x; i < npages; i += 256)
+      s_pages[i] = kv_page_id(a.kv_indices, rq.page_off, (first_page + i) << a.log2B, a.log2B,
+                              a.num_pages);
   }
 
   // ---- this lane's query row (column of S^T and O^T)
@@ -175,7 +174,6 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 
   const int nblk = (kv_end - kv_begin + BLK - 1) / BLK;
   const int nloc = wave < nblk ? (nblk - wave + kWaves - 1) / kWaves : 0;   // this wave's blocks
-  const int32_t bmask = (1 << a.log2B) - 1;
   const char* kbase = static_cast<const char*>(a.k_cache) + (int64_t)it.hk * a.k_sh * EB;
   const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh * EB;
   const int64_t kps = a.k_sp * EB, kbs = a.k_sb * EB, vps = a.v_sp * EB, vbs = a.v_sb * EB;
@@ -189,7 +187,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   // cache row of token t (clamped to the item) -> byte offset of its page/slot
   auto row_off = [&](int t, int64_t ps, int64_t bs) -> int64_t {
     t = min(t, kv_end - 1);
-    return (int64_t)s_pages[(t >> a.log2B) - first_page] * ps + (int64_t)(t & bmask) * bs;
+    return kv_row_offset(s_pages[kv_page_index(0, t, a.log2B) - first_page], t, a.log2B, ps, bs);
   };
   // issue the HBM reads of local block k (rows past the item are clamped, so a
   // prefetch past the last block reads valid memory).  When every K/V byte is

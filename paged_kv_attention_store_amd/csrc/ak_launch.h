@@ -21,9 +21,11 @@ struct StoreArgs {
 // src/dst dtypes are ak_dtype values.
 hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s);
 
+// addressing: 0 = the decode / fp32 kernels' row offsets, 1 = the prefill
+// kernels' copy offsets
 hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int32_t* kv_indices,
-                               int32_t R, int32_t log2B, int64_t num_pages, int64_t* slots,
-                               hipStream_t s);
+                               int32_t R, int32_t log2B, int64_t num_pages, int32_t addressing,
+                               int64_t* slots, hipStream_t s);
 
 hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t s);
 
@@ -44,13 +46,43 @@ hipError_t launch_slot_mapping(const int32_t* block_table, int64_t row_stride, c
                                const int32_t* seq_lens, int32_t R, int32_t B, int64_t* slot_mapping,
                                int64_t N, hipStream_t s);
 
-// Physical page holding KV position t of a request whose pages start at
-// kv_indices[page_off]; the position's row inside the page is t & (B - 1).
-// Page ids are clamped into the pool so a corrupt table cannot address outside it.
-__device__ __forceinline__ int64_t kv_page(const int32_t* __restrict__ kv_indices, int32_t page_off,
-                                           int32_t t, int32_t log2B, int64_t num_pages) {
-  int64_t page = (int64_t)kv_indices[page_off + (t >> log2B)];
-  return page < 0 ? 0 : (page >= num_pages ? num_pages - 1 : page);
+// ---- K/V row addressing shared by the attention kernels and ak_gather_slots
+// (which runs these same functions with page stride B and slot stride 1, so the
+// offset they produce is the flat cache slot page * B + t % B).
+
+// A page id clamped into the pool, so a corrupt table cannot address outside it.
+__device__ __forceinline__ int32_t clamp_page(int32_t page, int64_t num_pages) {
+  const int32_t pmax = (int32_t)min(num_pages - 1, (int64_t)INT32_MAX);
+  return min(max(page, 0), pmax);
+}
+
+// Index into kv_indices of the page holding KV position t of a request whose
+// page list starts at page_off.
+__device__ __forceinline__ int32_t kv_page_index(int32_t page_off, int32_t t, int32_t log2B) {
+  return page_off + (t >> log2B);
+}
+
+// The (clamped) physical page holding KV position t of a request.
+__device__ __forceinline__ int32_t kv_page_id(const int32_t* __restrict__ kv_indices, int32_t page_off,
+                                              int32_t t, int32_t log2B, int64_t num_pages) {
+  return clamp_page(kv_indices[kv_page_index(page_off, t, log2B)], num_pages);
+}
+
+// Offset of KV position t's row in page `page`, for a page stride and a slot
+// stride in any unit (bytes in the kernels).
+__device__ __forceinline__ int64_t kv_row_offset(int32_t page, int32_t t, int32_t log2B,
+                                                 int64_t page_stride, int64_t slot_stride) {
+  return (int64_t)page * page_stride + (int64_t)(t & ((1 << log2B) - 1)) * slot_stride;
+}
+
+// The same for the load-to-LDS copies, with the offset inside the page formed in
+// 32 bits (slot stride times the page size below 2 GiB, checked on the host) and
+// a byte offset within the row added to it.
+__device__ __forceinline__ uint64_t kv_copy_offset(uint32_t page, int32_t t, int32_t log2B,
+                                                   uint32_t page_stride, uint32_t slot_stride,
+                                                   uint32_t in_row) {
+  const uint32_t slot = (uint32_t)(t & ((1 << log2B) - 1));
+  return (uint64_t)page * page_stride + (slot * slot_stride + in_row);
 }
 
 }  // namespace ak

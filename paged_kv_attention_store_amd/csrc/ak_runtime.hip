@@ -1082,8 +1082,11 @@ extern "C" ak_status ak_plan_export(const ak_plan_t* p, int32_t* items, int64_t 
   return AK_OK;
 }
 
-extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* stream) {
+extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int32_t addressing, int64_t* slots,
+                                     void* stream) {
   if (!p || !slots) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: null argument");
+  if (addressing != 0 && addressing != 1)
+    return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: addressing must be 0 (decode) or 1 (prefill)");
   if (p->host_only) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: plan was built host-only");
   if (p->R == 0) return AK_OK;
   std::vector<int64_t> off(p->R, 0);
@@ -1099,7 +1102,7 @@ extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int64_t* slots, void* s
   if (e != hipSuccess) return hip_fail(e, "ak_gather_slots: hipMalloc");
   e = hipMemcpyAsync(d_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = launch_gather_slots(p->d_reqs, d_off, p->kv_indices, p->R, p->log2B, INT64_MAX >> 16,
+    e = launch_gather_slots(p->d_reqs, d_off, p->kv_indices, p->R, p->log2B, INT32_MAX, addressing,
                             slots, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(d_off);

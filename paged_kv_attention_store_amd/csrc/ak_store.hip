@@ -137,6 +137,10 @@ __global__ __launch_bounds__(256) void store_kv_kernel(StoreArgs a) {
   }
 }
 
+// The flat slot of every KV position of every request, through the addressing
+// functions the attention kernels use for their K/V rows, with page stride B and
+// slot stride 1 in place of the cache's byte strides.
+template <int ADDRESSING>
 __global__ __launch_bounds__(256) void gather_slots_kernel(const Req* __restrict__ reqs,
                                                            const int64_t* __restrict__ kv_off,
                                                            const int32_t* __restrict__ kv_indices,
@@ -144,9 +148,18 @@ __global__ __launch_bounds__(256) void gather_slots_kernel(const Req* __restrict
                                                            int64_t* __restrict__ slots) {
   const Req rq = reqs[blockIdx.y];
   const int64_t base = kv_off[blockIdx.y];
+  const int32_t B = 1 << log2B;
   for (int t = blockIdx.x * blockDim.x + threadIdx.x; t < rq.L; t += gridDim.x * blockDim.x) {
-    const int64_t page = kv_page(kv_indices, rq.page_off, t, log2B, num_pages);
-    slots[base + t] = (page << log2B) + (t & ((1 << log2B) - 1));
+    if (ADDRESSING == 0) {
+      // decode and fp32 kernels: clamped page id, then the row offset
+      const int32_t page = kv_page_id(kv_indices, rq.page_off, t, log2B, num_pages);
+      slots[base + t] = kv_row_offset(page, t, log2B, B, 1);
+    } else {
+      // prefill kernels: raw page id loaded ahead, clamped at the copy, copy offset
+      const int32_t raw = kv_indices[kv_page_index(rq.page_off, t, log2B)];
+      slots[base + t] = (int64_t)kv_copy_offset((uint32_t)clamp_page(raw, num_pages), t, log2B,
+                                                (uint32_t)B, 1u, 0u);
+    }
   }
 }
 
@@ -191,13 +204,18 @@ hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hip
 }
 
 hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int32_t* kv_indices,
-                               int32_t R, int32_t log2B, int64_t num_pages, int64_t* slots,
-                               hipStream_t s) {
+                               int32_t R, int32_t log2B, int64_t num_pages, int32_t addressing,
+                               int64_t* slots, hipStream_t s) {
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (R <= 0) return hipSuccess;
   dim3 grid(64, (unsigned)R);
-  hipLaunchKernelGGL(gather_slots_kernel, grid, dim3(256), 0, s, reqs, kv_off, kv_indices, log2B,
-                     num_pages, slots);
+  if (addressing == 0) {
+    hipLaunchKernelGGL(gather_slots_kernel<0>, grid, dim3(256), 0, s, reqs, kv_off, kv_indices,
+                       log2B, num_pages, slots);
+  } else {
+    hipLaunchKernelGGL(gather_slots_kernel<1>, grid, dim3(256), 0, s, reqs, kv_off, kv_indices,
+                       log2B, num_pages, slots);
+  }
   return hipGetLastError();
 }
 

@@ -13,15 +13,18 @@ from tests.gpu_harness import plan_for, say
 pytestmark = pytest.mark.gpu
 
 
+@pytest.mark.parametrize("addressing", [0, 1], ids=["decode_rows", "prefill_copies"])
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
-def test_gather_slots_bit_exact(k):
-    say(f"[indexing] config {k}")
+def test_gather_slots_bit_exact(k, addressing):
+    # the slots come from the kernels' own K/V addressing functions (page-id read,
+    # clamp, row offset) run with page stride B and slot stride 1
+    say(f"[indexing] config {k}, addressing {addressing}")
     wl = W.config(k)
     idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).cuda()
     plan = plan_for(wl, {"kv_indices": idx}, wl.windows[0])
     total = int(wl.kv_lens.sum())
     slots = torch.full((total,), -7, dtype=torch.int64, device="cuda")
-    ak.ak_gather_slots(plan, slots)
+    ak.ak_gather_slots(plan, slots, addressing=addressing)
     got = slots.cpu().numpy()
     exp = np.concatenate([M.request_slots(wl.kv_indptr, wl.kv_indices, wl.last_page_len,
                                           wl.page_size, r) for r in range(wl.batch_size)])
