@@ -29,7 +29,11 @@ Two optional legs measure the large-tile kernel alone: on long uniform prompts
 ("prefill_shapes") and the fixed and per-block cost of a 256-row segment
 ("segcost").
 
-The CPU baseline times the float64 oracle on a sample of the decode batch.
+The CPU baseline times the float64 oracle, after the GPU legs and in the same
+run, on a bounded sample of each of the five workloads (decode in GB/s of the
+same algorithmic bytes, extend in TFLOP/s of the same visible pairs, and tokens/s),
+with the threads it used and the host's CPU count; the headline carries the
+decode batch's figure, every other leg its own workload's.
 """
 
 from __future__ import annotations
@@ -225,8 +229,9 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     torch.cuda.synchronize()
     ak.ak_profile_enable(False)
     detail = ak.ak_profile_read()
-    # host cost of planning alone (the in-loop figure also holds any wait for a
-    # free workspace when the host runs ahead of the GPU)
+    # host cost of planning alone; the in-step ak_plan calls also hold any wait
+    # for a pooled workspace to come free when the host runs ahead of the GPU
+    # (its last runs still executing), reported as the difference
     t = time.perf_counter()
     for _ in range(20):
         for w in wl.windows:
@@ -241,8 +246,9 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     res = dict(wl=wl, ms_step=ms_step, gbs=step_bytes / (ms_step * 1e-3) / 1e9, prof=prof,
                tok_s_layer=wl.total_q / (ms_step * 1e-3 / n_layers),
                dec_bytes=dec_bytes, flops=flops,
-               info=ak.ak_plan_info(plans[0]), plan_us=plan_s / steps * 1e6,
+               info=ak.ak_plan_info(plans[0]), plan_call_us=plan_s / steps * 1e6,
                plan_host_us=plan_host_us,
+               plan_wait_us=max(0.0, plan_s / steps * 1e6 - plan_host_us),
                step_bytes=step_bytes, layers=n_layers)
     n, ms = prof["attn_small"]
     if n and dec_bytes:
@@ -267,7 +273,8 @@ def measure(ak, torch, dev, wl, n_layers, steps, warmup):
     if n:
         res["merge_avg_us"] = ms / n * 1e3
     msg = (f"[bench] {wl.name}: {ms_step:.3f} ms/step, step-level {res['gbs']:.1f} GB/s; "
-           f"plan {res['plan_us']:.1f} us (host only {res['plan_host_us']:.1f} us); ")
+           f"plan {res['plan_host_us']:.1f} us host + {res['plan_wait_us']:.1f} us waiting for a "
+           f"free workspace; ")
     if "small_gbs" in res:
         msg += f"attn_small {res['small_avg_ms'] * 1e3:.1f} us -> {res['small_gbs']:.1f} GB/s; "
     if "large_tflops" in res:
@@ -304,34 +311,87 @@ def copy_bandwidth(torch, dev, gib):
 
 # ------------------------------------------------------------ CPU baseline
 
-def cpu_baseline(wl, budget_s=12.0, n_req=16):
-    """The float64 oracle as it stands, on a sample of the decode batch."""
+# Bounded samples of each workload for the oracle (request indices, seconds of
+# timed passes).  The oracle's input generation is not timed.
+CPU_SAMPLES = {
+    1: ("all 4 decode requests", lambda wl: list(range(wl.batch_size)), 1.0),
+    2: ("16 of 64 decode requests", lambda wl: list(range(16)), 8.0),
+    3: ("2 of 8 extend requests", lambda wl: [0, 1], 6.0),
+    4: ("the 2048-token chunk (request 0) and 8 of 255 decode requests, full attention",
+        lambda wl: [0] + list(range(1, 9)), 8.0),
+    5: ("1 of 8 decode requests (131072 KV tokens)", lambda wl: [0], 4.0),
+}
+
+
+def _host_cores():
     import threadpoolctl
 
+    cpus = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return cpus, blas
+
+
+def _cpu_leg(wl, reqs, budget_s, what):
+    """Time the float64 oracle on `reqs` of `wl` (full attention) until `budget_s`
+    seconds of passes; its algorithmic work in the GPU metric's unit."""
     from oracle import metadata as M
     from oracle import workload_run as orun
 
-    reqs = list(range(n_req))
     kc, vc = orun.caches_after_store(wl)
     sl = np.concatenate([M.request_slots(wl.kv_indptr, wl.kv_indices, wl.last_page_len,
                                          wl.page_size, r) for r in reqs])
     kc.materialize(sl)          # input generation is not timed
     vc.materialize(sl)
     q = orun.decoded_q(wl)
-    kv_tok = int(wl.kv_lens[reqs].sum())
-    work = kv_tok * wl.num_kv_heads * wl.head_dim * 2 * 2 + n_req * wl.num_qo_heads * wl.head_dim * 4
     passes, t = 0, 0.0
-    while t < budget_s:
+    while t < budget_s or passes == 0:
         t0 = time.perf_counter()
         orun.run(wl, requests=reqs, caches=(kc, vc), q=q)
         t += time.perf_counter() - t0
         passes += 1
-    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
-    return {"value": round(work * passes / t / 1e9, 4), "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n_req} of {wl.batch_size} decode requests ({kv_tok} KV tokens), one layer, "
-                      f"{passes} passes in {t:.1f} s (same algorithmic-byte count as the GPU "
-                      f"metric); host cores available {len(os.sched_getaffinity(0))}"}
+    sub = dict(q_lens=wl.q_lens[reqs], kv_lens=wl.kv_lens[reqs])
+    tokens = int(sub["q_lens"].sum())
+    if what == "decode":
+        kv_tok = int(sub["kv_lens"].sum())
+        work = kv_tok * wl.num_kv_heads * wl.head_dim * 2 * EB[wl.kv_dtype] + \
+            tokens * wl.num_qo_heads * (wl.head_dim * EB[wl.q_dtype] * 2 + 4)
+        value, unit = work * passes / t / 1e9, "GB/s"
+    else:
+        pairs = sum(int(n) * (int(L) - int(n)) + int(n) * (int(n) + 1) // 2
+                    for n, L in zip(sub["q_lens"], sub["kv_lens"]))
+        work = 4.0 * wl.head_dim * wl.num_qo_heads * pairs
+        value, unit = work * passes / t / 1e12, "TFLOP/s"
+    return value, unit, tokens * passes / t, passes, t
+
+
+def cpu_baseline(k, wl=None):
+    """The float64 oracle as it stands on a bounded sample of workload k, in the
+    same algorithmic units as the GPU figure (decode GB/s, prefill TFLOP/s), on
+    the host cores of this machine."""
+    from synth import workloads as W
+
+    wl = W.config(k) if wl is None else wl
+    desc, pick, budget = CPU_SAMPLES[k]
+    reqs = pick(wl)
+    cpus, blas = _host_cores()
+    legs = []
+    if k == 4:
+        legs.append(("prefill", [reqs[0]], budget / 2))
+        legs.append(("decode", reqs[1:], budget / 2))
+    else:
+        legs.append(("prefill" if k == 3 else "decode", reqs, budget))
+    out = []
+    for what, rr, b in legs:
+        value, unit, tok_s, passes, t = _cpu_leg(wl, rr, b, what)
+        out.append({"value": round(value, 4), "unit": unit, "cores": int(blas), "host_cpus": cpus,
+                    "kind": "oracle", "phase": what,
+                    "tokens_per_s": round(tok_s, 2), "wall_s_per_pass": round(t / passes, 3),
+                    "sample": f"{wl.name}: {desc}; {what} part: requests {rr[:4]}"
+                              f"{'...' if len(rr) > 4 else ''}, one layer, {passes} passes in "
+                              f"{t:.1f} s; BLAS threads {blas} of {cpus} host CPUs"})
+        log(f"[bench] cpu baseline config {k} ({what}): {value:.4f} {unit}, "
+            f"{tok_s:.2f} tokens/s, {passes} passes in {t:.1f} s")
+    return out[0] if len(out) == 1 else {o["phase"]: o for o in out}
 
 
 # -------------------------------------------------------------------- main
@@ -609,7 +669,11 @@ def main():
             extra[name] = measure_segcost(ak, torch, dev)
             continue
         extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(dec["wl"])
+    # the oracle on a bounded sample of every workload (configs 1-5), after the
+    # GPU legs, in this same run
+    cpu_by = {} if args.no_cpu_baseline else {k: cpu_baseline(k) for k in (1, 2, 3, 4, 5)}
+    cpu = cpu_by.get(2)
+    leg_config = {"prefill": 3, "mixed": 4, "longfp8": 5}
     traffic = measured_traffic()
     wl = dec["wl"]
     line = {
@@ -632,8 +696,8 @@ def main():
             "layers": args.layers,
             "kv_tokens": int(wl.kv_lens.sum()),
             "bytes_per_step": dec["step_bytes"],
-            "plan_us": round(dec["plan_us"], 1),
             "plan_host_us": round(dec["plan_host_us"], 1),
+            "plan_wait_us": round(dec["plan_wait_us"], 1),
             "plan": dec["info"],
         },
         "roofline": {
@@ -648,6 +712,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": cpu,
+        "cpu_baseline_by_config": {str(k): v for k, v in cpu_by.items()},
         "copy_GBs": copy,
         "tokens_per_s_per_layer": round(dec["tok_s_layer"], 1),
     }
@@ -656,8 +721,8 @@ def main():
             line[name] = r
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),
-             "layers": r["layers"], "step_GBs": round(r["gbs"], 1), "plan_us": round(r["plan_us"], 1),
-             "plan_host_us": round(r["plan_host_us"], 1),
+             "layers": r["layers"], "step_GBs": round(r["gbs"], 1),
+             "plan_host_us": round(r["plan_host_us"], 1), "plan_wait_us": round(r["plan_wait_us"], 1),
              "tokens_per_s_per_layer": round(r["tok_s_layer"], 1)}
         if "small_gbs" in r:
             e["decode"] = {"kernel": "attn_small", "achieved": round(r["small_gbs"], 1),
@@ -675,6 +740,8 @@ def main():
             e["merge_avg_us"] = round(r["merge_avg_us"], 2)
         if "combined_frac" in r:
             e["combined_roofline_frac"] = round(r["combined_frac"], 4)
+        if name in leg_config and leg_config[name] in cpu_by:
+            e["cpu_baseline"] = cpu_by[leg_config[name]]
         line[name] = e
     print(json.dumps(line), flush=True)
 

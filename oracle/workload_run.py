@@ -16,6 +16,12 @@ from . import attention as A
 
 
 class GeneratedCache:
+    # slots generated per piece; large requests are generated piece by piece on a
+    # few host threads (NumPy releases the interpreter lock inside its array
+    # operations), which changes nothing in the codes, only the wall time
+    piece_slots = 8192
+    threads = 8
+
     def __init__(self, wl: W.Workload, which: str):
         self.wl = wl
         self.which = which
@@ -39,6 +45,19 @@ class GeneratedCache:
         codes = self.codes_at(slots)
         self._pre_slots, self._pre_codes = slots, codes
 
+    def _generated(self, slots: np.ndarray) -> np.ndarray:
+        """Pool codes at these slots as generated (before this step's store)."""
+        n, k = len(slots), self.piece_slots
+        if n <= k:
+            return A.encode(W.pool_values(self.wl, self.which, slots), self.dtype, self.scale)
+        import concurrent.futures
+
+        pieces = [slots[i:i + k] for i in range(0, n, k)]
+        with concurrent.futures.ThreadPoolExecutor(self.threads) as ex:
+            parts = list(ex.map(lambda sl: A.encode(W.pool_values(self.wl, self.which, sl),
+                                                    self.dtype, self.scale), pieces))
+        return np.concatenate(parts)
+
     def codes_at(self, slots) -> np.ndarray:
         slots = np.asarray(slots, dtype=np.int64)
         pre = getattr(self, "_pre_slots", None)
@@ -47,10 +66,11 @@ class GeneratedCache:
             pos = np.clip(pos, 0, len(pre) - 1)
             if np.all(pre[pos] == slots):
                 return self._pre_codes[pos]
-        base = A.encode(W.pool_values(self.wl, self.which, slots), self.dtype, self.scale)
-        for i, s in enumerate(slots):
-            if int(s) in self.overlay:
-                base[i] = self.overlay[int(s)]
+        base = self._generated(slots)
+        if self.overlay:
+            keys = np.fromiter(self.overlay.keys(), dtype=np.int64, count=len(self.overlay))
+            for i in np.nonzero(np.isin(slots, keys))[0]:
+                base[i] = self.overlay[int(slots[i])]
         return base
 
     def decode_slots(self, slots) -> np.ndarray:

@@ -146,11 +146,13 @@ def _torch_table(device, dtype: str):
     return _TORCH_TABLES[key]
 
 
-def fill_torch(out, seed: int, stream: str, start: int = 0, chunk: int = 1 << 25) -> None:
+def fill_torch(out, seed: int, stream: str, start: int = 0, chunk: int = 1 << 27) -> None:
     """Fill a contiguous torch tensor with values at counters start .. start+numel.
 
     out.dtype must be torch.float32 (f32 grid) or torch.bfloat16 (bf16 grid).
-    Works on any device; chunks bound the int64 temporaries.
+    Works on any device.  Each chunk is 45 elementwise launches on a GPU; chunks
+    bound the int64 temporaries (a few GB at the default 2^27 elements) and keep
+    the launch count low (a multi-GB pool takes tens of chunks, not hundreds).
     """
     import torch
 

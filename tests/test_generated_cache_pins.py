@@ -51,8 +51,11 @@ def _stores(wl, rng):
     return [(v1, s1), (v2, s2)]
 
 
+@pytest.mark.parametrize("piece", [8192, 7])
 @pytest.mark.parametrize("qd,kd", DTYPES, ids=[f"{a}-{b}" for a, b in DTYPES])
-def test_generated_cache_equals_whole_pool_store(qd, kd):
+def test_generated_cache_equals_whole_pool_store(qd, kd, piece, monkeypatch):
+    # piece = 7: slots generated in many pieces on several threads
+    monkeypatch.setattr(orun.GeneratedCache, "piece_slots", piece)
     wl = W.custom(seed=41, q_lens=[1, 5, 1, 3], kv_lens=[37, 64, 9, 130], page_size=16,
                   num_qo_heads=8, num_kv_heads=2, head_dim=64, q_dtype=qd, kv_dtype=kd,
                   spare_pages=4)
