@@ -22,9 +22,10 @@ batch ("prefill": large-tile kernel TFLOP/s against the bf16 dense MFMA peak),
 the mixed chunked-prefill + decode step with full and sliding-window layers
 ("mixed"), the fp8 long-context decode ("longfp8"), decode requests sharing
 a 4096-token prefix run plainly (with the shared-pages flag, and streamed) and
-as a cascade ("cascade"), and decode issued eagerly and as a replayed graph
+as a cascade ("cascade"), decode issued eagerly and as a replayed graph
 over a fixed plan, on a small batch ("graph") and on the 64-request batch
-above ("graph64").
+above ("graph64"), and the decode and fp8 long-decode attention with the
+split-KV plan against the stream-K plan ("streamk").
 Two optional legs measure the large-tile kernel alone: on long uniform prompts
 ("prefill_shapes") and the fixed and per-block cost of a 256-row segment
 ("segcost").
@@ -542,6 +543,51 @@ def measure_graph(ak, torch, dev, wl, n_layers, steps, warmup, merge_in_kernel=T
     return res
 
 
+def measure_stream_k(ak, torch, dev, launches=20):
+    """Decode attention with the default split-KV plan and with the stream-K plan
+    (equal contiguous shares of the decode KV, persistent workgroups) on the
+    64-request decode batch and the fp8 long decode: average kernel time over
+    `launches` runs alternating two layers' caches, HIP events on the stream."""
+    from synth import workloads as W
+
+    out = {}
+    for k in (2, 5):
+        wl = W.config(k)
+        layers = make_layers(wl, 2, dev)
+        idx = torch.from_numpy(wl.kv_indices.astype(np.int32)).to(dev)
+        res = {}
+        for name, kw in (("split_kv", {}), ("stream_k", {"stream_k": True})):
+            plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, idx, wl.last_page_len, wl.num_qo_heads,
+                              wl.num_kv_heads, wl.head_dim, wl.page_size, **kw)
+            for L in layers:
+                ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"],
+                          k_scale=wl.kv_scale, v_scale=wl.kv_scale)
+            torch.cuda.synchronize()
+            ak.ak_profile_read()
+            ak.ak_profile_enable(True, kinds=["attn_small", "merge"])
+            for i in range(launches):
+                L = layers[i % 2]
+                ak.ak_run(plan, L["q"], L["kc"], L["vc"], out=L["out"], lse=L["lse"],
+                          k_scale=wl.kv_scale, v_scale=wl.kv_scale)
+            torch.cuda.synchronize()
+            ak.ak_profile_enable(False)
+            pr = ak.ak_profile_read()
+            us = pr["attn_small"][1] / pr["attn_small"][0] * 1e3
+            mus = pr["merge"][1] / max(1, pr["merge"][0]) * 1e3
+            info = ak.ak_plan_info(plan)
+            res[name] = {"attn_us": round(us, 1), "merge_us": round(mus, 2),
+                         "GBs": round(decode_bytes(wl) / ((us + mus) * 1e-6) / 1e9, 1),
+                         "items": info["small_items"], "partial_rows": info["partial_rows"]}
+            if name == "stream_k":
+                res[name]["workgroups"] = info["stream_k_workgroups"]
+        out[wl.name] = res
+        log(f"[bench] {wl.name}: split-KV {res['split_kv']['attn_us']} + {res['split_kv']['merge_us']} us, "
+            f"stream-K {res['stream_k']['attn_us']} + {res['stream_k']['merge_us']} us")
+        del layers
+        torch.cuda.empty_cache()
+    return out
+
+
 def time_large(ak, torch, dev, wl, launches=20):
     """Average duration (us) of the large-tile attention kernel on `wl`, HIP events
     around every launch, two layers with their own caches alternating."""
@@ -623,6 +669,7 @@ WORKLOADS = {
     "graph64": (lambda W: W.config(2), 32),
     "prefill_shapes": (None, 2),
     "segcost": (None, 2),
+    "streamk": (None, 2),
 }
 
 
@@ -632,9 +679,9 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=32, help="layers of the headline decode step")
-    ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph,graph64",
+    ap.add_argument("--also", default="prefill,mixed,longfp8,cascade,graph,graph64,streamk",
                     help="comma list of further workloads: prefill,mixed,longfp8,cascade,graph,"
-                         "graph64 (default), prefill_shapes, segcost ('' for none)")
+                         "graph64,streamk (default), prefill_shapes, segcost ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-gib", type=float, default=1.0,
                     help="size of the device-to-device copy timed as bandwidth context (0: skip)")
@@ -667,6 +714,9 @@ def main():
             continue
         if name == "segcost":
             extra[name] = measure_segcost(ak, torch, dev)
+            continue
+        if name == "streamk":
+            extra[name] = measure_stream_k(ak, torch, dev)
             continue
         extra[name] = measure(ak, torch, dev, fac(W), nl, max(2, args.steps), 2)
     # the oracle on a bounded sample of every workload (configs 1-5), after the
@@ -717,7 +767,7 @@ def main():
         "tokens_per_s_per_layer": round(dec["tok_s_layer"], 1),
     }
     for name, r in extra.items():
-        if name in ("cascade", "graph", "graph64", "prefill_shapes", "segcost"):
+        if name in ("cascade", "graph", "graph64", "prefill_shapes", "segcost", "streamk"):
             line[name] = r
             continue
         e = {"workload": r["wl"].name, "ms_per_step": round(r["ms_step"], 4),

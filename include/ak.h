@@ -179,10 +179,18 @@ enum {
                                    their parts inside the attention kernel (bf16 q) instead
                                    of by a separate merge launch: one launch fewer per run,
                                    for launch-bound small batches; slower for large ones  */
-  AK_PLAN_SHARED_PAGES = 4      /* requests of the batch share pages (a common prefix): decode
+  AK_PLAN_SHARED_PAGES = 4,     /* requests of the batch share pages (a common prefix): decode
                                    reads K/V with ordinary cached loads so later readers of a
                                    shared page hit the caches; by default they are streamed
                                    (read once, kept out of the caches)                    */
+  AK_PLAN_STREAM_K = 8          /* stream-K decode ("SGLang attention backend", the lean-decode
+                                   metadata of "Other backends' metadata"): the decode units'
+                                   KV ranges, laid end to end, are cut into equal contiguous
+                                   shares, one per resident workgroup (two per compute
+                                   unit); each workgroup of one persistent launch works
+                                   through the pieces of its share, and a unit cut across
+                                   shares is merged from their partial states.  Not for
+                                   fixed plans                                             */
 };
 
 typedef struct {
@@ -194,7 +202,7 @@ typedef struct {
                             size 1 or 2 with long contexts)                        */
   int32_t min_chunk;     /* smallest KV split in tokens; 0 = library default       */
   int32_t flags;         /* AK_PLAN_HOST_ONLY | AK_PLAN_MERGE_IN_KERNEL |
-                            AK_PLAN_SHARED_PAGES                                     */
+                            AK_PLAN_SHARED_PAGES | AK_PLAN_STREAM_K                  */
   void* stream;          /* stream for the plan's upload; NULL = default stream     */
 } ak_plan_opts;
 
@@ -393,14 +401,22 @@ ak_status ak_plan_update(ak_plan_t* plan, const int32_t* qo_indptr, const int32_
                          const int32_t* last_page_len, int32_t batch_size, void* stream);
 
 /* ak_plan_info -- host-side summary of a plan (any plan, host-only included).
- * Writes up to 12 int64 values into `info` (caller-owned host array):
+ * Writes up to 13 int64 values into `info` (caller-owned host array):
  *   [0] batch_size  [1] total query rows T  [2] work items  [3] small-tile items
  *   [4] large-tile items  [5] split (request, KV head) units  [6] merge jobs
  *   [7] partial rows in the split workspace; for a fixed plan the capacities
  *   [8] small-tile items [9] large-tile items [10] merge jobs [11] partial rows
- *   (0 for other plans).
+ *   (0 for other plans); [12] stream-K workgroups (0 for other plans).
  * Errors: AK_ERR_INVALID_ARG. */
 ak_status ak_plan_info(const ak_plan_t* plan, int64_t* info, int32_t n);
+
+/* ak_plan_workgroups -- a stream-K plan's workgroup table, for checking: host
+ * int32 wg_first[P + 1] such that workgroup g of the decode launch runs the small
+ * items wg_first[g] .. wg_first[g+1]-1 (in ak_plan_export's order, small items
+ * first).  *count receives P + 1 (0 for plans without AK_PLAN_STREAM_K); a
+ * `capacity` below it returns AK_ERR_INVALID_ARG.  Errors: AK_ERR_INVALID_ARG. */
+ak_status ak_plan_workgroups(const ak_plan_t* plan, int32_t* wg_first, int64_t capacity,
+                             int64_t* count);
 
 /* ak_plan_export -- copy the plan's work list to host memory for checking.
  * Each item is 8 int32: request, kv_head, first row, row count, kv_begin,

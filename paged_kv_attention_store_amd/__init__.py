@@ -45,13 +45,15 @@ AK_F32, AK_BF16, AK_FP8_E4M3, AK_I32, AK_I64 = 0, 1, 2, 3, 4
 AK_PLAN_HOST_ONLY = 1
 AK_PLAN_MERGE_IN_KERNEL = 2
 AK_PLAN_SHARED_PAGES = 4
+AK_PLAN_STREAM_K = 8
 AK_PROFILE_ALL = 0x1F
 
 EXPORTED = ["ak_store_kv", "ak_plan", "ak_plan_destroy", "ak_run", "ak_last_error",
             "ak_plan_info", "ak_plan_export", "ak_gather_slots", "ak_profile_enable",
             "ak_merge_states", "ak_csr_from_block_table", "ak_slot_mapping", "ak_plan_fixed",
             "ak_plan_update",
-            "ak_profile_read", "ak_version", "ak_fp8_to_bf16", "ak_run_noalloc"]
+            "ak_profile_read", "ak_version", "ak_fp8_to_bf16", "ak_run_noalloc",
+            "ak_plan_workgroups"]
 
 
 class AkError(RuntimeError):
@@ -109,6 +111,8 @@ def _load():
     lib.ak_plan_info.restype = ctypes.c_int
     lib.ak_plan_export.argtypes = [ctypes.c_void_p, i32p, ctypes.c_int64, P(ctypes.c_int64), i32p]
     lib.ak_plan_export.restype = ctypes.c_int
+    lib.ak_plan_workgroups.argtypes = [ctypes.c_void_p, i32p, ctypes.c_int64, P(ctypes.c_int64)]
+    lib.ak_plan_workgroups.restype = ctypes.c_int
     lib.ak_merge_states.argtypes = [P(AkTensor)] * 6 + [ctypes.c_void_p]
     lib.ak_merge_states.restype = ctypes.c_int
     vp, i64 = ctypes.c_void_p, ctypes.c_int64
@@ -246,10 +250,10 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
             head_dim: int, page_size: int, causal: bool = True, window: int = -1,
             sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
             min_chunk: int = 0, host_only: bool = False, merge_in_kernel: bool = False,
-            shared_pages: bool = False, stream=None) -> Plan:
+            shared_pages: bool = False, stream_k: bool = False, stream=None) -> Plan:
     """Build a plan.  qo_indptr, kv_indptr and last_page_len are host arrays
     (anything NumPy accepts); kv_indices is a device int32 tensor (or None for a
-    host-only plan)."""
+    host-only plan).  stream_k selects the stream-K decode partition."""
     qo, qo_p = _host_i32(qo_indptr)
     kv, kv_p = _host_i32(kv_indptr)
     last, last_p = _host_i32(last_page_len)
@@ -263,7 +267,8 @@ def ak_plan(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads: int, 
     opts.min_chunk = int(min_chunk)
     opts.flags = ((AK_PLAN_HOST_ONLY if host_only else 0) |
                   (AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
-                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0) |
+                  (AK_PLAN_STREAM_K if stream_k else 0))
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None:
@@ -285,7 +290,8 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
                   window: int = -1, sm_scale: float | None = None, num_cus: int = 0,
                   max_splits: int = 0, min_chunk: int = 0, host_only: bool = False,
                   max_pages: int | None = None, max_query_len: int = 0,
-                  merge_in_kernel: bool = False, shared_pages: bool = False, stream=None) -> Plan:
+                  merge_in_kernel: bool = False, shared_pages: bool = False, stream_k: bool = False,
+                  stream=None) -> Plan:
     """A plan with a fixed device workspace for graph capture.  kv_indices is the
     stable device int32 buffer later batches write their page ids into (its size
     is the page capacity); host-only plans take None and max_pages.  max_query_len
@@ -297,7 +303,8 @@ def ak_plan_fixed(max_batch: int, max_tokens: int, kv_indices, num_qo_heads: int
     opts.min_chunk = int(min_chunk)
     opts.flags = ((AK_PLAN_HOST_ONLY if host_only else 0) |
                   (AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
-                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0) |
+                  (AK_PLAN_STREAM_K if stream_k else 0))
     opts.stream = None if host_only else _stream_ptr(stream)
     idx_ptr = None
     if kv_indices is not None and not host_only:
@@ -410,12 +417,22 @@ def ak_merge_states(o_a, lse_a, o_b, lse_b, out=None, lse_out=None, stream=None)
 
 
 def ak_plan_info(plan: Plan) -> dict:
-    buf = (ctypes.c_int64 * 12)()
-    _check(_lib.ak_plan_info(plan.handle, buf, 12))
+    buf = (ctypes.c_int64 * 13)()
+    _check(_lib.ak_plan_info(plan.handle, buf, 13))
     keys = ["batch_size", "total_q", "items", "small_items", "large_items", "split_units",
             "merge_jobs", "partial_rows", "cap_small_items", "cap_large_items", "cap_merge_jobs",
-            "cap_partial_rows"]
+            "cap_partial_rows", "stream_k_workgroups"]
     return dict(zip(keys, [int(x) for x in buf]))
+
+
+def ak_plan_workgroups(plan: Plan) -> np.ndarray:
+    """A stream-K plan's workgroup table wg_first (int32 [P + 1]; empty otherwise)."""
+    n = ak_plan_info(plan)["stream_k_workgroups"]
+    buf = np.zeros(max(n + 1, 1), dtype=np.int32)
+    cnt = ctypes.c_int64()
+    _check(_lib.ak_plan_workgroups(plan.handle, buf.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                   len(buf), ctypes.byref(cnt)))
+    return buf[:cnt.value]
 
 
 def ak_plan_export(plan: Plan):

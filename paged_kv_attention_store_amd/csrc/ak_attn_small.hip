@@ -100,24 +100,33 @@ __device__ __forceinline__ u32x4 kv_load(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
 
-template <int D, bool FP8, bool STREAM>
-__global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
+// LDS of one workgroup: the waves' V stages, reused by the 4-wave combine
+template <int D, bool FP8>
+struct SmallLds {
+  using S = Shape<D, FP8>;
+  static constexpr int ORW = D + 4;          // floats per row of the combine buffer
+  static constexpr int STAGE_BYTES = kWaves * S::STAGE * 2;
+  static constexpr int COMB_BYTES = (2 * kWaves * 16 + kWaves * 16 * ORW) * 4;
+  static constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
+};
+
+// One work item (a KV range of one decode-shaped unit) on one workgroup.
+// `smem`, `s_pages` and `s_last` are the workgroup's LDS, `tid` the thread's
+// index in the workgroup; every thread returns from here with no barrier
+// pending, and the caller separates two items run by one workgroup with a
+// barrier (the next item reuses the LDS).
+template <int D, bool FP8, bool STREAM, bool PERSIST>
+__device__ __forceinline__ void small_item(const AttnArgs& a, const Item& it,
+                                           unsigned char (&smem)[SmallLds<D, FP8>::SMEM],
+                                           int32_t (&s_pages)[kSmallMaxPages], int32_t& s_last,
+                                           int tid) {
   using S = Shape<D, FP8>;
   constexpr int BLK = S::BLK, NT = S::NT, NSTEP = S::NSTEP, NDT = S::NDT, EB = S::EB;
   constexpr int KL = S::KL, CPR = S::CPR, TPI = S::TPI, VL = S::VL, VROW = S::VROW;
-  constexpr int ORW = D + 4;          // floats per row of the combine buffer
-  constexpr int STAGE_BYTES = kWaves * S::STAGE * 2;
-  constexpr int COMB_BYTES = (2 * kWaves * 16 + kWaves * 16 * ORW) * 4;
-  constexpr int SMEM = STAGE_BYTES > COMB_BYTES ? STAGE_BYTES : COMB_BYTES;
-  __shared__ __align__(16) unsigned char smem[SMEM];
-  __shared__ int32_t s_pages[kSmallMaxPages];
-  __shared__ int32_t s_last;   // this workgroup finished its unit's last part
-
-  const Item it = a.items[blockIdx.x];
-  if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
+  constexpr int ORW = SmallLds<D, FP8>::ORW;
   const Req rq = a.reqs[it.r];
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
   const int n16 = lane & 15;
   const int g4 = lane >> 4;
   const int G = a.G;
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   const int first_page = kv_begin >> a.log2B;
   {
     const int npages = ((kv_end - 1) >> a.log2B) - first_page + 1;   // <= kSmallMaxPages (plan)
-    for (int i = threadIdx.x; i < npages; i += 256)
+    for (int i = tid; i < npages; i += 256)
       s_pages[i] = kv_page_id(a.kv_indices, rq.page_off, (first_page + i) << a.log2B, a.log2B,
                               a.num_pages);
   }
@@ -341,7 +350,9 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   // waits stay exact: each compute waits only for its own block.  (A third
   // register set does not fit beside bf16 D = 128 operands without spills.)
   if (nloc > 0) {
-    constexpr bool kThree = FP8 || D == 64;
+    // (the persistent loop of a stream-K launch holds a little more live state,
+    // which two sets leave room for with fp8 rows at D = 128)
+    constexpr bool kThree = (FP8 || D == 64) && !(PERSIST && FP8 && D == 128);
     Regs ra, rb, rc;
     issue(ra, 0);
     if (kThree) {
@@ -387,8 +398,8 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   __syncthreads();
 
   constexpr int CPT = D / 16;   // columns per thread
-  const int row = threadIdx.x >> 4;
-  const int c0 = (threadIdx.x & 15) * CPT;
+  const int row = tid >> 4;
+  const int c0 = (tid & 15) * CPT;
   const bool active = row < it.nrows;
   float M = -INFINITY;
 #pragma unroll
@@ -421,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
     const int rhead = it.hk * G + (rrho - rj * G);
     const int64_t rtok = (int64_t)rq.q_off + rj;
     store_row_bf16<CPT>(static_cast<uint16_t*>(a.out) + rtok * a.o_st + (int64_t)rhead * a.o_sh + c0, o);
-    if (a.lse && (threadIdx.x & 15) == 0) a.lse[rtok * a.l_st + (int64_t)rhead * a.l_sh] = lse2 * kLn2;
+    if (a.lse && (tid & 15) == 0) a.lse[rtok * a.l_st + (int64_t)rhead * a.l_sh] = lse2 * kLn2;
     return;
   }
   // ---- a split unit's parts are merged by whichever workgroup finishes last.
@@ -439,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < CPT; cc += 4)
       *reinterpret_cast<f32x4*>(pp + cc) = f32x4{o[cc], o[cc + 1], o[cc + 2], o[cc + 3]};
-    if ((threadIdx.x & 15) == 0) a.part_lse[prow] = lse2;
+    if ((tid & 15) == 0) a.part_lse[prow] = lse2;
     return;
   }
   if (active) {
@@ -448,19 +459,19 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
     for (int cc = 0; cc < CPT; ++cc)
       __hip_atomic_store(pp + cc, o[cc], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if ((threadIdx.x & 15) == 0)
+    if ((tid & 15) == 0)
       __hip_atomic_store(a.part_lse + prow, lse2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __builtin_amdgcn_s_waitcnt(kVmcntZero);   // this thread's partial stores are complete
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int parts = a.merges[it.merge0].count;
     s_last = __hip_atomic_fetch_add(a.counters + it.merge0, 1, __ATOMIC_RELAXED,
                                     __HIP_MEMORY_SCOPE_AGENT) == parts - 1;
   }
   __syncthreads();
   if (!s_last) return;
-  if (threadIdx.x == 0)
+  if (tid == 0)
     __hip_atomic_store(a.counters + it.merge0, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (!active) return;
   // The row's 16 lanes read its parts' LSEs 16 at a time and reduce the max in
@@ -468,8 +479,8 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
   // the weighted sum takes by a lane broadcast, summing the parts in order with
   // four part rows in flight (the same arithmetic as one part at a time).
   const MergeJob jb = a.merges[it.merge0 + row];
-  const int sub = threadIdx.x & 15;          // lane within the row's group
-  const int grp = threadIdx.x & 48;          // first lane of the group in the wave
+  const int sub = tid & 15;          // lane within the row's group
+  const int grp = tid & 48;          // first lane of the group in the wave
   auto lse_of = [&](int s) {
     return __hip_atomic_load(a.part_lse + jb.pfirst + (int64_t)s * jb.pstride, __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
@@ -518,31 +529,68 @@ __global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
 #pragma unroll
   for (int cc = 0; cc < CPT; ++cc) o[cc] *= inv;
   store_row_bf16<CPT>(static_cast<uint16_t*>(a.out) + (int64_t)jb.token * a.o_st + (int64_t)jb.head * a.o_sh + c0, o);
-  if (a.lse && (threadIdx.x & 15) == 0)
+  if (a.lse && (tid & 15) == 0)
     a.lse[(int64_t)jb.token * a.l_st + (int64_t)jb.head * a.l_sh] =
         wsum > 0.f ? (m + log2f(wsum)) * kLn2 : -INFINITY;
+}
+
+// One workgroup per item, or (PERSIST, stream-K plans) one persistent
+// workgroup per share running its items in order.
+template <int D, bool FP8, bool STREAM, bool PERSIST>
+__global__ __launch_bounds__(256, 2) void attn_small_kernel(AttnArgs a) {
+  __shared__ __align__(16) unsigned char smem[SmallLds<D, FP8>::SMEM];
+  __shared__ int32_t s_pages[kSmallMaxPages];
+  __shared__ int32_t s_last;   // this workgroup finished its unit's last part
+  if constexpr (PERSIST) {
+    const int first = a.wg_first[blockIdx.x], last = a.wg_first[blockIdx.x + 1];
+    for (int i = first; i < last; ++i) {
+      const Item it = a.items[i];
+      // the thread index is re-derived per item from a value the compiler cannot
+      // see through, so nothing computed from it is hoisted out of the loop and
+      // kept live across items (that would cost the item body its registers)
+      int tid = threadIdx.x;
+      asm volatile("" : "+v"(tid));
+      small_item<D, FP8, STREAM, true>(a, it, smem, s_pages, s_last, tid);
+      __syncthreads();   // the next item reuses the LDS
+    }
+  } else {
+    const Item it = a.items[blockIdx.x];
+    if (it.nrows == 0) return;   // padding item (uniform over the workgroup)
+    small_item<D, FP8, STREAM, false>(a, it, smem, s_pages, s_last, (int)threadIdx.x);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, bool shared_pages,
-                             hipStream_t s) {
+                             int n_wg, hipStream_t s) {
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
-  dim3 grid((unsigned)n_items);
-#define AK_SMALL_CASE(DD, F8)                                                                \
-  if (D == DD && kv_dtype == (F8 ? AK_FP8_E4M3 : AK_BF16)) {                                 \
-    if (shared_pages)                                                                        \
-      hipLaunchKernelGGL((attn_small_kernel<DD, F8, false>), grid, dim3(256), 0, s, a);      \
-    else                                                                                     \
-      hipLaunchKernelGGL((attn_small_kernel<DD, F8, true>), grid, dim3(256), 0, s, a);       \
-    return hipGetLastError();                                                                \
+  const bool persist = n_wg > 0;
+  dim3 grid((unsigned)(persist ? n_wg : n_items));
+#define AK_SMALL_LAUNCH(DD, F8, ST, PE) \
+  hipLaunchKernelGGL((attn_small_kernel<DD, F8, ST, PE>), grid, dim3(256), 0, s, a)
+#define AK_SMALL_CASE(DD, F8)                                                 \
+  if (D == DD && kv_dtype == (F8 ? AK_FP8_E4M3 : AK_BF16)) {                  \
+    if (persist) {                                                            \
+      if (shared_pages)                                                       \
+        AK_SMALL_LAUNCH(DD, F8, false, true);                                 \
+      else                                                                    \
+        AK_SMALL_LAUNCH(DD, F8, true, true);                                  \
+    } else {                                                                  \
+      if (shared_pages)                                                       \
+        AK_SMALL_LAUNCH(DD, F8, false, false);                                \
+      else                                                                    \
+        AK_SMALL_LAUNCH(DD, F8, true, false);                                 \
+    }                                                                         \
+    return hipGetLastError();                                                 \
   }
   AK_SMALL_CASE(128, false)
   AK_SMALL_CASE(64, false)
   AK_SMALL_CASE(128, true)
   AK_SMALL_CASE(64, true)
 #undef AK_SMALL_CASE
+#undef AK_SMALL_LAUNCH
   return hipErrorInvalidValue;
 }
 

@@ -123,6 +123,7 @@ struct AttnArgs {
   float* part_lse;     // [partial_rows], log2 domain
   const MergeJob* merges;  // split small units' merge jobs (Item::merge0 indexes them)
   int32_t* counters;   // arrival counter per split small unit, at Item::merge0
+  const int32_t* wg_first;   // stream-K: workgroup g runs small items wg_first[g] .. wg_first[g+1]-1
   int64_t q_st, q_sh;  // q strides (elements): token, head
   int64_t o_st, o_sh;
   int64_t l_st, l_sh;

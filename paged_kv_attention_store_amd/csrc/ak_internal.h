@@ -22,6 +22,10 @@ constexpr int kSegCost = 3;       // start-up cost of a large-tile segment, in t
 constexpr int kMinPartTiles = 8;  // smallest KV part a large tile job is split into, in tiles
 constexpr double kTileBytes = 4.0e6;  // bytes the whole GPU streams in one large-tile time
 constexpr int kPartsPerCu = 6;    // decode KV parts per compute unit the split aims at
+constexpr int kStreamKPerCu = 4;  // stream-K shares per compute unit: two rounds of its two
+                                  // resident decode workgroups (measured: with one round of
+                                  // two, every workgroup starts at once and the long fp8
+                                  // decode is 18% slower)
 
 struct Item {          // one workgroup's work; 48 bytes
   int32_t r;           // request
@@ -78,6 +82,10 @@ struct ak_plan_t {
   int64_t small_merges = 0;           // jobs of split small units
   bool merge_in_kernel = false;       // small units merged inside the small-tile kernel
   bool shared_pages = false;          // requests share pages: cached (not streaming) K/V reads
+  // stream-K decode: small items are grouped by persistent workgroup; workgroup g
+  // runs small items wg_first[g] .. wg_first[g+1]-1
+  bool stream_k = false;
+  std::vector<int32_t> wg_first;
   int64_t partial_rows = 0;
   int64_t split_units = 0;
   // fixed plan: capacities the workspace is sized for (kernels are launched over
@@ -96,6 +104,7 @@ struct ak_plan_t {
   ak::MergeJob* d_merges = nullptr;
   ak::MergeJob* d_merges_large = nullptr;   // large jobs' merge list
   int32_t* d_counters = nullptr;            // arrival counters of split small units
+  int32_t* d_wg_first = nullptr;            // stream-K: first small item of each workgroup
   float* d_part_o = nullptr;
   float* d_part_lse = nullptr;
   int device = 0;

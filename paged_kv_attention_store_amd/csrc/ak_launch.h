@@ -30,8 +30,10 @@ hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int
 hipError_t launch_fp8_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t s);
 
 // kv dtype: AK_BF16 or AK_FP8_E4M3 for bf16 queries.
+// n_wg > 0: a persistent launch of n_wg workgroups, each running its items
+// a.wg_first[g] .. a.wg_first[g+1]-1 (stream-K plans); else one workgroup per item.
 hipError_t launch_attn_small(const AttnArgs& a, int n_items, int D, int kv_dtype, bool shared_pages,
-                             hipStream_t s);
+                             int n_wg, hipStream_t s);
 hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int n_items, int D, hipStream_t s);
 

@@ -80,6 +80,8 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
       (opts && opts->min_chunk > 0) ? round_up(opts->min_chunk, kKvAlign) : 256;
   p->merge_in_kernel = opts && (opts->flags & AK_PLAN_MERGE_IN_KERNEL);
   p->shared_pages = opts && (opts->flags & AK_PLAN_SHARED_PAGES);
+  p->stream_k = opts && (opts->flags & AK_PLAN_STREAM_K);
+  p->wg_first.clear();
 
   // ---- lengths and validation
   p->kv_lens.assign(R, 0);
@@ -155,115 +157,188 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     }
   }
 
-  // Split size: about kPartsPerCu KV chunks per compute unit over the whole batch,
-  // between min_chunk and 4096 tokens, in multiples of kKvAlign.
-  int64_t chunk = ceil_div(std::max<int64_t>(small_tokens, 1), (int64_t)p->num_cus * kPartsPerCu);
-  chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
-  chunk = std::max<int64_t>(chunk, min_chunk);
-
-  // Units longest first (partial rows and merge jobs follow this order).
-  std::vector<int32_t> order(small.size());
-  for (size_t i = 0; i < small.size(); ++i) order[i] = (int32_t)i;
-  std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-    const int32_t lx = small[x].hi - small[x].lo, ly = small[y].hi - small[y].lo;
-    return lx != ly ? lx > ly : x < y;
-  });
-  p->merges.reserve((size_t)small.size() * kSmallRows);
-  // parts are at least chunk / kGuideFloor tokens (or min_chunk)
-  p->small_items.reserve(small.size() +
-                         (size_t)(small_tokens / std::max<int64_t>(min_chunk, chunk / kGuideFloor)) + 16);
-
   int64_t prow = 0;
   int64_t split_units = 0;
-  // Guided part size: the units come longest first, and each is cut into parts of
-  // about (decode KV still to cut) / (kGuideShare * CUs) tokens, between
-  // chunk / kGuideFloor and chunk.  Parts shrink toward the end of the grid, so
-  // its last round holds short items and the compute units run out of work
-  // nearly together.
-  int64_t w_rem = small_tokens;
-  const int64_t t_floor = std::max<int64_t>(min_chunk, round_up(chunk / kGuideFloor, kKvAlign));
-  for (int32_t ui : order) {
-    const Unit& u = small[ui];
-    const int64_t len = (int64_t)u.hi - u.lo;
-    int64_t t = round_up(ceil_div(std::max<int64_t>(w_rem, 1), kGuideShare * (int64_t)p->num_cus), kKvAlign);
-    t = std::min<int64_t>(chunk, std::max<int64_t>(t, t_floor));
-    w_rem -= len;
-    // S parts with boundaries on a kKvAlign grid anchored below lo, each the grid
-    // point nearest to an equal share (parts differ by at most kKvAlign tokens;
-    // at least kKvAlign tokens per share keeps every part non-empty)
-    const int64_t base = (u.lo / kKvAlign) * kKvAlign;
-    const int64_t ext = (int64_t)u.hi - base;
-    int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, t)));
-    for (;;) {
-      S = std::max<int64_t>(1, std::min<int64_t>(S, ext / kKvAlign));
-      // every part must fit a small tile's page table (only binds for tiny pages)
-      const int64_t span = S <= 1 ? (((int64_t)u.hi - 1) >> p->log2B) - (u.lo >> p->log2B) + 1
-                                  : (ceil_div(ext, S) + kKvAlign + B - 1) / B + 1;
-      if (span <= kSmallMaxPages) break;
-      S = std::max<int64_t>(S + 1, ceil_div(S * span, kSmallMaxPages - 1));
-    }
-    const int64_t nparts = S;
-    auto bound = [&](int64_t s) -> int64_t {
-      if (s <= 0) return u.lo;
-      if (s >= nparts) return u.hi;
-      return std::max<int64_t>(u.lo, base + (s * ext + nparts * (kKvAlign / 2)) / (nparts * kKvAlign) * kKvAlign);
+  if (p->stream_k) {
+    // Stream-K: the units' visible KV ranges laid end to end, in unit order, are
+    // cut into P equal contiguous shares (cuts on the kKvAlign grid of each
+    // unit's positions), one per persistent workgroup; a share's intersection with
+    // a unit is one piece (an item), pieces longer than a small tile's page table
+    // are cut again, and a unit left in several pieces is merged from their
+    // partial states like any split unit.  Items are grouped by workgroup.
+    const int64_t P = (int64_t)p->num_cus * kStreamKPerCu;
+    const int64_t share =
+        std::max<int64_t>(kKvAlign, round_up(ceil_div(std::max<int64_t>(small_tokens, 1), P), kKvAlign));
+    const int64_t max_piece =
+        std::max<int64_t>(kKvAlign, ((int64_t)(kSmallMaxPages - 2) * B) / kKvAlign * kKvAlign);
+    struct Piece {
+      int32_t unit, a, b, wg;
     };
-    if (nparts <= 1) {
-      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0, -1, {}});
-      continue;
-    }
-    const int64_t ubase = prow;
-    // the unit's first merge job, which a part merging in-kernel starts from
-    const int32_t m0 = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
-    int32_t a = (int32_t)bound(0);
-    for (int64_t s = 0; s < nparts; ++s) {
-      const int32_t b = (int32_t)bound(s + 1);
-      p->small_items.push_back(
-          Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0, m0, {}});
-      a = b;
-    }
-    const Req& q = p->reqs[u.r];
-    for (int32_t rho = 0; rho < u.rows; ++rho) {
-      MergeJob m{};
-      m.token = q.q_off + (rho >> lgG);
-      m.head = u.hk * G + (rho & (G - 1));
-      m.pfirst = (int32_t)(ubase + rho);
-      m.pstride = u.rows;
-      m.count = (int32_t)nparts;
-      p->merges.push_back(m);
-    }
-    prow += nparts * u.rows;
-    ++split_units;
-    if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
-  }
-  p->small_merges = (int64_t)p->merges.size();
-  // Launch order: longest KV range first over all items (a unit's parts are equal
-  // slices of it, so unit order alone leaves long items behind short ones), so
-  // the dispatcher's earliest-free order approximates longest-processing-time
-  // scheduling and the grid ends on the shortest items.  Partial rows, merge jobs
-  // and arrival counters are indexed explicitly, so the order is free.
-  {
-    // a stable counting sort by length when the lengths span a short range (the
-    // usual case: parts are at most the 4096-token chunk), else a comparison sort
-    const size_t n = p->small_items.size();
-    int32_t lmax = 0;
-    for (const Item& x : p->small_items) lmax = std::max(lmax, x.kv_end - x.kv_begin);
-    std::vector<Item> sorted(n);
-    if ((size_t)lmax <= 4 * n + 65536) {
-      std::vector<int32_t> start((size_t)lmax + 2, 0);
-      for (const Item& x : p->small_items) ++start[(size_t)(lmax - (x.kv_end - x.kv_begin)) + 1];
-      for (size_t k = 1; k < start.size(); ++k) start[k] += start[k - 1];
-      for (const Item& x : p->small_items) sorted[(size_t)start[(size_t)(lmax - (x.kv_end - x.kv_begin))]++] = x;
-    } else {
-      std::vector<uint64_t> key(n);
-      for (size_t i = 0; i < n; ++i) {
-        const Item& x = p->small_items[i];
-        key[i] = ((uint64_t)(uint32_t)(lmax - (x.kv_end - x.kv_begin)) << 32) | (uint64_t)i;
+    std::vector<Piece> pieces;
+    pieces.reserve(small.size() + (size_t)P * 2);
+    std::vector<int32_t> npieces(small.size(), 0);
+    int64_t flat = 0;   // flattened position of the current unit's first key
+    for (size_t ui = 0; ui < small.size(); ++ui) {
+      const Unit& u = small[ui];
+      int64_t pos = u.lo;
+      for (;;) {
+        const int64_t g = std::min<int64_t>(P - 1, (flat + pos - u.lo) / share);
+        int64_t b = u.hi;
+        if (g < P - 1) {   // this share ends at flattened (g + 1) * share
+          const int64_t end = (int64_t)u.lo + (g + 1) * share - flat;
+          b = std::min<int64_t>(b, std::max<int64_t>(pos + 1, round_up(end, kKvAlign)));
+        }
+        b = std::min<int64_t>(b, pos + max_piece);
+        pieces.push_back(Piece{(int32_t)ui, (int32_t)pos, (int32_t)b, (int32_t)g});
+        ++npieces[ui];
+        pos = b;
+        if (pos >= u.hi) break;
       }
-      std::sort(key.begin(), key.end());
-      for (size_t i = 0; i < n; ++i) sorted[i] = p->small_items[(size_t)(key[i] & 0xFFFFFFFFu)];
+      flat += (int64_t)u.hi - u.lo;
     }
-    p->small_items.swap(sorted);
+    // partial rows and merge jobs of units left in several pieces
+    std::vector<int64_t> ubase(small.size(), -1);
+    std::vector<int32_t> umerge(small.size(), -1);
+    for (size_t ui = 0; ui < small.size(); ++ui) {
+      if (npieces[ui] <= 1) continue;
+      const Unit& u = small[ui];
+      ubase[ui] = prow;
+      umerge[ui] = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
+      const Req& q = p->reqs[u.r];
+      for (int32_t rho = 0; rho < u.rows; ++rho) {
+        MergeJob m{};
+        m.token = q.q_off + (rho >> lgG);
+        m.head = u.hk * G + (rho & (G - 1));
+        m.pfirst = (int32_t)(prow + rho);
+        m.pstride = u.rows;
+        m.count = npieces[ui];
+        p->merges.push_back(m);
+      }
+      prow += (int64_t)npieces[ui] * u.rows;
+      ++split_units;
+      if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
+    }
+    p->small_items.reserve(pieces.size());
+    p->wg_first.assign((size_t)P + 1, 0);
+    std::vector<int32_t> seen(small.size(), 0);
+    for (const Piece& pc : pieces) {
+      const Unit& u = small[(size_t)pc.unit];
+      const int32_t k = seen[(size_t)pc.unit]++;
+      const int32_t pb = ubase[(size_t)pc.unit] < 0 ? -1 : (int32_t)(ubase[(size_t)pc.unit] + (int64_t)k * u.rows);
+      p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, pc.a, pc.b, pb, 0, umerge[(size_t)pc.unit], {}});
+      ++p->wg_first[(size_t)pc.wg + 1];
+    }
+    for (int64_t g = 0; g < P; ++g) p->wg_first[(size_t)g + 1] += p->wg_first[(size_t)g];
+    p->small_merges = (int64_t)p->merges.size();
+  } else {
+    // Split size: about kPartsPerCu KV chunks per compute unit over the whole batch,
+    // between min_chunk and 4096 tokens, in multiples of kKvAlign.
+    int64_t chunk = ceil_div(std::max<int64_t>(small_tokens, 1), (int64_t)p->num_cus * kPartsPerCu);
+    chunk = std::min<int64_t>(std::max<int64_t>(round_up(chunk, kKvAlign), min_chunk), 4096);
+    chunk = std::max<int64_t>(chunk, min_chunk);
+
+    // Units longest first (partial rows and merge jobs follow this order).
+    std::vector<int32_t> order(small.size());
+    for (size_t i = 0; i < small.size(); ++i) order[i] = (int32_t)i;
+    std::sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      const int32_t lx = small[x].hi - small[x].lo, ly = small[y].hi - small[y].lo;
+      return lx != ly ? lx > ly : x < y;
+    });
+    p->merges.reserve((size_t)small.size() * kSmallRows);
+    // parts are at least chunk / kGuideFloor tokens (or min_chunk)
+    p->small_items.reserve(small.size() +
+                           (size_t)(small_tokens / std::max<int64_t>(min_chunk, chunk / kGuideFloor)) + 16);
+
+    // Guided part size: the units come longest first, and each is cut into parts of
+    // about (decode KV still to cut) / (kGuideShare * CUs) tokens, between
+    // chunk / kGuideFloor and chunk.  Parts shrink toward the end of the grid, so
+    // its last round holds short items and the compute units run out of work
+    // nearly together.
+    int64_t w_rem = small_tokens;
+    const int64_t t_floor = std::max<int64_t>(min_chunk, round_up(chunk / kGuideFloor, kKvAlign));
+    for (int32_t ui : order) {
+      const Unit& u = small[ui];
+      const int64_t len = (int64_t)u.hi - u.lo;
+      int64_t t = round_up(ceil_div(std::max<int64_t>(w_rem, 1), kGuideShare * (int64_t)p->num_cus), kKvAlign);
+      t = std::min<int64_t>(chunk, std::max<int64_t>(t, t_floor));
+      w_rem -= len;
+      // S parts with boundaries on a kKvAlign grid anchored below lo, each the grid
+      // point nearest to an equal share (parts differ by at most kKvAlign tokens;
+      // at least kKvAlign tokens per share keeps every part non-empty)
+      const int64_t base = (u.lo / kKvAlign) * kKvAlign;
+      const int64_t ext = (int64_t)u.hi - base;
+      int64_t S = std::min<int64_t>(max_splits, std::max<int64_t>(1, ceil_div(len, t)));
+      for (;;) {
+        S = std::max<int64_t>(1, std::min<int64_t>(S, ext / kKvAlign));
+        // every part must fit a small tile's page table (only binds for tiny pages)
+        const int64_t span = S <= 1 ? (((int64_t)u.hi - 1) >> p->log2B) - (u.lo >> p->log2B) + 1
+                                    : (ceil_div(ext, S) + kKvAlign + B - 1) / B + 1;
+        if (span <= kSmallMaxPages) break;
+        S = std::max<int64_t>(S + 1, ceil_div(S * span, kSmallMaxPages - 1));
+      }
+      const int64_t nparts = S;
+      auto bound = [&](int64_t s) -> int64_t {
+        if (s <= 0) return u.lo;
+        if (s >= nparts) return u.hi;
+        return std::max<int64_t>(u.lo, base + (s * ext + nparts * (kKvAlign / 2)) / (nparts * kKvAlign) * kKvAlign);
+      };
+      if (nparts <= 1) {
+        p->small_items.push_back(Item{u.r, u.hk, 0, u.rows, u.lo, u.hi, -1, 0, -1, {}});
+        continue;
+      }
+      const int64_t ubase = prow;
+      // the unit's first merge job, which a part merging in-kernel starts from
+      const int32_t m0 = p->merge_in_kernel ? (int32_t)p->merges.size() : -1;
+      int32_t a = (int32_t)bound(0);
+      for (int64_t s = 0; s < nparts; ++s) {
+        const int32_t b = (int32_t)bound(s + 1);
+        p->small_items.push_back(
+            Item{u.r, u.hk, 0, u.rows, a, b, (int32_t)(ubase + s * u.rows), 0, m0, {}});
+        a = b;
+      }
+      const Req& q = p->reqs[u.r];
+      for (int32_t rho = 0; rho < u.rows; ++rho) {
+        MergeJob m{};
+        m.token = q.q_off + (rho >> lgG);
+        m.head = u.hk * G + (rho & (G - 1));
+        m.pfirst = (int32_t)(ubase + rho);
+        m.pstride = u.rows;
+        m.count = (int32_t)nparts;
+        p->merges.push_back(m);
+      }
+      prow += nparts * u.rows;
+      ++split_units;
+      if (prow > INT32_MAX / 2) return fail(AK_ERR_UNSUPPORTED, "ak_plan: split workspace too large");
+    }
+    p->small_merges = (int64_t)p->merges.size();
+    // Launch order: longest KV range first over all items (a unit's parts are equal
+    // slices of it, so unit order alone leaves long items behind short ones), so
+    // the dispatcher's earliest-free order approximates longest-processing-time
+    // scheduling and the grid ends on the shortest items.  Partial rows, merge jobs
+    // and arrival counters are indexed explicitly, so the order is free.
+    {
+      // a stable counting sort by length when the lengths span a short range (the
+      // usual case: parts are at most the 4096-token chunk), else a comparison sort
+      const size_t n = p->small_items.size();
+      int32_t lmax = 0;
+      for (const Item& x : p->small_items) lmax = std::max(lmax, x.kv_end - x.kv_begin);
+      std::vector<Item> sorted(n);
+      if ((size_t)lmax <= 4 * n + 65536) {
+        std::vector<int32_t> start((size_t)lmax + 2, 0);
+        for (const Item& x : p->small_items) ++start[(size_t)(lmax - (x.kv_end - x.kv_begin)) + 1];
+        for (size_t k = 1; k < start.size(); ++k) start[k] += start[k - 1];
+        for (const Item& x : p->small_items) sorted[(size_t)start[(size_t)(lmax - (x.kv_end - x.kv_begin))]++] = x;
+      } else {
+        std::vector<uint64_t> key(n);
+        for (size_t i = 0; i < n; ++i) {
+          const Item& x = p->small_items[i];
+          key[i] = ((uint64_t)(uint32_t)(lmax - (x.kv_end - x.kv_begin)) << 32) | (uint64_t)i;
+        }
+        std::sort(key.begin(), key.end());
+        for (size_t i = 0; i < n; ++i) sorted[i] = p->small_items[(size_t)(key[i] & 0xFFFFFFFFu)];
+      }
+      p->small_items.swap(sorted);
+    }
   }
   // ---- large tiles: one workgroup per segment, launched longest first so the
   // dispatcher's earliest-free-CU order approximates longest-processing-time

@@ -409,9 +409,10 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     // arrival counters of split small units, uploaded as zeros (each run leaves
     // them at zero again)
     const size_t b_cnt = align256((size_t)p->small_merges * sizeof(int32_t));
+    const size_t b_wg = align256(p->wg_first.size() * sizeof(int32_t));
     const size_t b_po = align256((size_t)p->partial_rows * p->D * sizeof(float));
     const size_t b_pl = align256((size_t)p->partial_rows * sizeof(float));
-    const size_t meta = b_req + b_small + b_large + b_merge + b_cnt;
+    const size_t meta = b_req + b_small + b_large + b_merge + b_cnt + b_wg;
     p->d_bytes = meta + b_po + b_pl;
     if (p->d_bytes > 0) {
       st = acquire_ws(dev, p->d_bytes, meta, &p->ws);
@@ -427,6 +428,8 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
       p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
       p->d_merges_large = p->d_merges + p->small_merges;
       p->d_counters = reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge);
+      p->d_wg_first = b_wg ? reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge + b_cnt)
+                           : nullptr;
       p->d_part_o = reinterpret_cast<float*>(base + meta);
       p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
       unsigned char* h = static_cast<unsigned char*>(p->ws.host);
@@ -439,6 +442,9 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
         std::memcpy(h + b_req + b_small + b_large, p->merges.data(),
                     p->merges.size() * sizeof(MergeJob));
       if (b_cnt) std::memset(h + b_req + b_small + b_large + b_merge, 0, b_cnt);
+      if (b_wg)
+        std::memcpy(h + b_req + b_small + b_large + b_merge + b_cnt, p->wg_first.data(),
+                    p->wg_first.size() * sizeof(int32_t));
       hipStream_t s = opts ? static_cast<hipStream_t>(opts->stream) : nullptr;
       hipError_t e = hipSuccess;
       if (meta > 0) e = hipMemcpyAsync(p->d_buf, h, meta, hipMemcpyHostToDevice, s);
@@ -515,6 +521,8 @@ extern "C" ak_status ak_plan_fixed(int32_t max_batch, int64_t max_tokens, int64_
   if (max_tokens > INT32_MAX / 64 || max_pages > INT32_MAX)
     return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: capacity too large");
   const bool host_only = opts && (opts->flags & AK_PLAN_HOST_ONLY);
+  if (opts && (opts->flags & AK_PLAN_STREAM_K))
+    return fail(AK_ERR_UNSUPPORTED, "ak_plan_fixed: stream-K plans are not fixed-capacity");
   auto* p = new_plan();
   if (!p) return fail(AK_ERR_OOM, "ak_plan_fixed: out of host memory");
   int dev = 0;
@@ -772,6 +780,7 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
   a.part_o = p->d_part_o;
   a.merges = p->d_merges;
   a.counters = p->d_counters;
+  a.wg_first = p->stream_k ? p->d_wg_first : nullptr;
   a.part_lse = p->d_part_lse;
   a.q_st = q->stride[0];
   a.q_sh = q->stride[1];
@@ -820,7 +829,8 @@ extern "C" ak_status ak_run(const ak_plan_t* p, const ak_tensor* q, const ak_ten
     if (ns > 0) {
       a.items = p->d_small;
       ProfScope ps(1, s);
-      e = launch_attn_small(a, ns, p->D, kd, p->shared_pages, s);
+      e = launch_attn_small(a, ns, p->D, kd, p->shared_pages,
+                            p->stream_k ? (int)p->wg_first.size() - 1 : 0, s);
     }
     if (e != hipSuccess) return hip_fail(e, "ak_run: small-tile attention");
   }
@@ -986,9 +996,10 @@ extern "C" ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_
   const size_t b_large = align256(p->large_items.size() * sizeof(Item));
   const size_t b_merge = align256(p->merges.size() * sizeof(MergeJob));
   const size_t b_cnt = align256((size_t)p->small_merges * sizeof(int32_t));
+  const size_t b_wg = align256(p->wg_first.size() * sizeof(int32_t));
   const size_t b_po = align256((size_t)p->partial_rows * p->D * sizeof(float));
   const size_t b_pl = align256((size_t)p->partial_rows * sizeof(float));
-  const size_t meta = b_req + b_small + b_large + b_merge + b_cnt;
+  const size_t meta = b_req + b_small + b_large + b_merge + b_cnt + b_wg;
   if (st == AK_OK && meta + b_po + b_pl > kScratchBytes) {
     std::ostringstream os;
     os << "ak_run_noalloc: the batch's work list and split partials need " << meta + b_po + b_pl
@@ -1009,6 +1020,8 @@ extern "C" ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_
   p->d_merges = reinterpret_cast<MergeJob*>(base + b_req + b_small + b_large);
   p->d_merges_large = p->d_merges + p->small_merges;
   p->d_counters = reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge);
+  p->d_wg_first = b_wg ? reinterpret_cast<int32_t*>(base + b_req + b_small + b_large + b_merge + b_cnt)
+                       : nullptr;
   p->d_part_o = reinterpret_cast<float*>(base + meta);
   p->d_part_lse = reinterpret_cast<float*>(base + meta + b_po);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1031,6 +1044,9 @@ extern "C" ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_
       std::memcpy(hp + b_req + b_small, p->large_items.data(), p->large_items.size() * sizeof(Item));
     if (!p->merges.empty())
       std::memcpy(hp + b_req + b_small + b_large, p->merges.data(), p->merges.size() * sizeof(MergeJob));
+    if (b_wg)
+      std::memcpy(hp + b_req + b_small + b_large + b_merge + b_cnt, p->wg_first.data(),
+                  p->wg_first.size() * sizeof(int32_t));
     // from pageable memory: the host buffer is free for reuse once the call returns
     e = hipMemcpyAsync(base, hp, meta, hipMemcpyHostToDevice, s);
     if (e != hipSuccess) {
@@ -1049,7 +1065,7 @@ extern "C" const char* ak_last_error(void) { return g_err.c_str(); }
 
 extern "C" ak_status ak_plan_info(const ak_plan_t* p, int64_t* info, int32_t n) {
   if (!p || !info || n < 0) return fail(AK_ERR_INVALID_ARG, "ak_plan_info: null argument");
-  const int64_t v[12] = {p->R,
+  const int64_t v[13] = {p->R,
                         p->T,
                         (int64_t)(p->small_items.size() + p->large_items.size()),
                         (int64_t)p->small_items.size(),
@@ -1060,8 +1076,9 @@ extern "C" ak_status ak_plan_info(const ak_plan_t* p, int64_t* info, int32_t n) 
                         p->caps.small,
                         p->caps.large,
                         p->caps.merges_small + p->caps.merges_large,
-                        p->caps.partial_rows};
-  for (int i = 0; i < n && i < 12; ++i) info[i] = v[i];
+                        p->caps.partial_rows,
+                        p->stream_k ? (int64_t)p->wg_first.size() - 1 : 0};
+  for (int i = 0; i < n && i < 13; ++i) info[i] = v[i];
   return AK_OK;
 }
 
@@ -1079,6 +1096,17 @@ extern "C" ak_status ak_plan_export(const ak_plan_t* p, int32_t* items, int64_t 
       std::memcpy(o, &it, 8 * sizeof(int32_t));   // the eight public fields
       o += 8;
     }
+  return AK_OK;
+}
+
+extern "C" ak_status ak_plan_workgroups(const ak_plan_t* p, int32_t* wg_first, int64_t capacity,
+                                        int64_t* count) {
+  if (!p || !count) return fail(AK_ERR_INVALID_ARG, "ak_plan_workgroups: null argument");
+  const int64_t n = (int64_t)p->wg_first.size();
+  *count = n;
+  if (n > capacity || (n > 0 && !wg_first))
+    return fail(AK_ERR_INVALID_ARG, "ak_plan_workgroups: buffer too small");
+  if (n > 0) std::memcpy(wg_first, p->wg_first.data(), (size_t)n * sizeof(int32_t));
   return AK_OK;
 }
 
