@@ -77,3 +77,39 @@ def test_merge_in_kernel_across_layers_resets_counters():
         o2, l2 = run(wl, d, plain, q=q)
         assert _agree(o1, o2), f"layer {layer}"
         assert float((l1 - l2).abs().max()) <= 1e-5
+
+
+@pytest.mark.parametrize("stream_k", [False, True], ids=["split_kv", "stream_k"])
+def test_merge_in_kernel_publication_back_to_back(stream_k):
+    # The merging workgroup reads the other parts' partial rows after counting
+    # itself in; a part whose rows were not yet visible would hand it the previous
+    # run's rows.  Runs alternate two query sets and are enqueued back to back
+    # without a host synchronisation, so the partial buffers always hold the
+    # other query set's rows from the run before: every run must still equal the
+    # separate merge launch on its own queries.
+    wl = W.llama8b_decode(seed=7, R=12)
+    d = prepare(wl)
+    kw = dict(stream_k=True, num_cus=64) if stream_k else dict(min_chunk=64, num_cus=512)
+    fused = plan_for(wl, d, -1, merge_in_kernel=True, **kw)
+    plain = plan_for(wl, d, -1, **kw)
+    info = ak.ak_plan_info(fused)
+    say(f"[merge-in-kernel] back-to-back, {info}")
+    assert info["split_units"] > 0
+    qs = []
+    for s in (300, 301):
+        q = torch.empty_like(d["q"])
+        R.fill_torch(q, s, "q")
+        qs.append(q)
+    refs = [run(wl, d, plain, q=q) for q in qs]
+    outs = []
+    for i in range(40):
+        q = qs[i % 2]
+        o = torch.empty_like(q)
+        lse = torch.empty(wl.total_q, wl.num_qo_heads, dtype=torch.float32, device=q.device)
+        ak.ak_run(fused, q, d["k_cache"], d["v_cache"], out=o, lse=lse)
+        outs.append((o, lse))
+    torch.cuda.synchronize()
+    for i, (o, lse) in enumerate(outs):
+        ro, rl = refs[i % 2]
+        assert _agree(o, ro), f"run {i}"
+        assert float((lse - rl).abs().max()) <= 1e-5, f"run {i}"
