@@ -365,7 +365,7 @@ def ak_run_noalloc(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads
                    causal: bool = True, window: int = -1, k_scale: float = 1.0, v_scale: float = 1.0,
                    sm_scale: float | None = None, num_cus: int = 0, max_splits: int = 0,
                    min_chunk: int = 0, merge_in_kernel: bool = False, shared_pages: bool = False,
-                   stream=None):
+                   stream_k: bool = False, stream=None):
     """Plan and run one layer without any allocation by the library (its split
     workspace is a fixed device array); out (and lse) must be given."""
     qo, qo_p = _host_i32(qo_indptr)
@@ -380,7 +380,8 @@ def ak_run_noalloc(qo_indptr, kv_indptr, kv_indices, last_page_len, num_qo_heads
     opts.max_splits = int(max_splits)
     opts.min_chunk = int(min_chunk)
     opts.flags = ((AK_PLAN_MERGE_IN_KERNEL if merge_in_kernel else 0) |
-                  (AK_PLAN_SHARED_PAGES if shared_pages else 0))
+                  (AK_PLAN_SHARED_PAGES if shared_pages else 0) |
+                  (AK_PLAN_STREAM_K if stream_k else 0))
     idx_ptr = None
     if kv_indices is not None and kv_indices.numel():
         import torch

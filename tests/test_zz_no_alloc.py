@@ -57,6 +57,15 @@ def test_noalloc_equals_plan_and_run_two_calls(merge_in_kernel):
     _same_as_plan_and_run(small, d, -1, min_chunk=64, num_cus=512, **kw)
 
 
+def test_noalloc_stream_k():
+    # a stream-K plan's workgroup table travels in the same array
+    wl = W.llama8b_decode(seed=2, R=8)
+    say(f"[noalloc] stream-K {wl.name}")
+    d = prepare(wl)
+    _same_as_plan_and_run(wl, d, -1, stream_k=True, num_cus=16)
+    _same_as_plan_and_run(wl, d, -1, stream_k=True, merge_in_kernel=True)
+
+
 def test_noalloc_fp8_and_fp32():
     for wl in (W.llama70b_long_decode(seed=5, R=2, L=20000), W.config(1)):
         say(f"[noalloc] {wl.name}")
