@@ -8,8 +8,10 @@
 // head-group fusion figure of "Why metadata is built once per step" (query
 // heads of one KV head share every K/V byte, so they form one tile).
 //
-// gfx950 mapping.  One workgroup (4 waves) per work item; wave w takes the
-// item's blocks w, w+4, ... (16 tokens for bf16 rows, 32 for fp8 rows).  The
+// gfx950 mapping.  One workgroup (4 waves) per work item (or, for a stream-K
+// plan, one persistent workgroup per equal share of the batch's decode KV, running
+// the share's items one after the other); wave w takes the item's blocks w,
+// w+4, ... (16 tokens for bf16 rows, 32 for fp8 rows).  The
 // item's page ids are staged once in LDS.  Each wave runs a register pipeline:
 // the K and V rows of the next block (bf16, D = 128) or next two blocks (fp8
 // rows, D = 64) are in flight into spare register sets while block k is
