@@ -439,10 +439,12 @@ ak_status ak_plan_export(const ak_plan_t* plan, int32_t* items, int64_t capacity
  * 1 instead of the cache's byte strides: `addressing` 0 selects the decode and
  * fp32 kernels' form (page id clamped as staged, 64-bit row offset), 1 the
  * prefill kernels' load-to-LDS copy form (raw page id clamped at the copy,
- * in-page offset in 32 bits).  `slots` is a device int64 array of at least
- * sum_r L_r entries; the call synchronises the stream.  Errors:
- * AK_ERR_INVALID_ARG (null argument, host-only plan, addressing not 0 or 1),
- * AK_ERR_HIP. */
+ * in-page offset in 32 bits), 2 the same copy form computed entirely in 32 bits
+ * with 24-bit multiplies, which the prefill kernels use for pools of at most 2^24
+ * pages whose bytes (from a head's base) span at most 4 GiB (page ids are clamped
+ * into 2^24 pages here).  `slots` is a device int64 array of at least sum_r L_r
+ * entries; the call synchronises the stream.  Errors: AK_ERR_INVALID_ARG (null
+ * argument, host-only plan, addressing not 0, 1 or 2), AK_ERR_HIP. */
 ak_status ak_gather_slots(const ak_plan_t* plan, int32_t addressing, int64_t* slots, void* stream);
 
 /* ak_fp8_to_bf16 -- the cache's FP8 E4M3 decode, materialised (diagnostics).

@@ -451,7 +451,8 @@ def ak_plan_export(plan: Plan):
 
 def ak_gather_slots(plan: Plan, slots, addressing: int = 0, stream=None) -> None:
     """Write every request's KV slots (device int64 tensor of sum L entries) through
-    the decode kernels' (addressing 0) or the prefill kernels' (1) row addressing."""
+    the decode kernels' (addressing 0) or the prefill kernels' row addressing (1; 2 for
+    its 32-bit form)."""
     _check(_lib.ak_gather_slots(plan.handle, int(addressing), ctypes.c_void_p(slots.data_ptr()),
                                 _stream_ptr(stream)))
 

@@ -124,12 +124,18 @@ struct LargeTile {
     vr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);  // column within a 32-column d-tile
   }
 
+  // Copy instruction i of wave w carries the block's 16-byte chunks
+  // (8i + w)*64 .. (8i + w)*64 + 63, i.e. whole rows of 64 / CPRC consecutive
+  // tokens; consecutive instructions of a wave are 8 such groups apart, so a
+  // token's position modulo 16 (which the LDS swizzles depend on) is the same in
+  // every instruction of a lane.
+  __device__ __forceinline__ int copy_chunk0(int i) const { return (i * 8 + wave) * 64; }
   // KV position copied by this lane in copy instruction i of block b, when a
-  // block's rows are CPRC 16-byte chunks each and a wave issues NIC instructions
-  // (clamped into the segment's range, so a copy past its end reads valid memory)
+  // block's rows are CPRC 16-byte chunks each (clamped into the segment's range,
+  // so a copy past its end reads valid memory)
   template <int CPRC, int NIC>
   __device__ __forceinline__ int copy_token(int b, int i) const {
-    return min(it.kv_begin + b * KB + ((wave * NIC + i) * 64 + lane) / CPRC, it.kv_end - 1);
+    return min(it.kv_begin + b * KB + (copy_chunk0(i) + lane) / CPRC, it.kv_end - 1);
   }
   // page ids of this wave's copied tokens of block b, as stored (clamped when used)
   template <int CPRC, int NIC>
@@ -275,10 +281,12 @@ struct LargeTile {
 
   // ---- Q rows.  Each wave copies its 32 rows HBM -> LDS with the load-to-LDS path
   // (whole rows per instruction, 16 bytes per lane), rows 0-15 into q_lo and 16-31
-  // into q_hi at this wave's copy region (NI KB of each), chunk c of row r at slot
-  // c ^ (r mod CPR); rows past the tile's end fetch its last row (never stored).
-  // Loaded by the lane that owns the row, a load instruction would touch 32 rows
-  // 32 bytes at a time.
+  // into q_hi at this wave's copy region (the NI 1 KB pieces its own block copies
+  // fill: piece i at chunk copy_chunk0(i), QPI = 512 / D rows each), chunk c of row
+  // r at slot c ^ (r mod CPR); rows past the tile's end fetch its last row (never
+  // stored).  Loaded by the lane that owns the row, a load instruction would touch
+  // 32 rows 32 bytes at a time.
+  static constexpr int QPI = 512 / D;   // Q rows per 1 KB piece
   static_assert(16 * 2 * D == NI * 1024, "a wave's Q half-tile fills its copy region");
   __device__ __forceinline__ void issue_q(__bf16 (&q_lo)[TILE], __bf16 (&q_hi)[TILE]) const {
 #pragma unroll
@@ -293,14 +301,14 @@ struct LargeTile {
                             ((int64_t)rq.q_off + (rho_c >> lgG)) * a.q_st +
                             (int64_t)(it.hk * G + (rho_c & (G - 1))) * a.q_sh +
                             8 * (j ^ (r & (CPR - 1)));
-        __bf16* dst = (pt ? q_hi : q_lo) + 512 * (wave * NI + i);
+        __bf16* dst = (pt ? q_hi : q_lo) + 8 * copy_chunk0(i);
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
                                          (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
       }
   }
   __device__ __forceinline__ void read_q(const __bf16 (&q_lo)[TILE], const __bf16 (&q_hi)[TILE]) {
     const int r = n32 & 15;
-    const __bf16* qs = (n32 < 16 ? q_lo : q_hi) + 512 * wave * NI + r * D;
+    const __bf16* qs = (n32 < 16 ? q_lo : q_hi) + 8 * copy_chunk0(r / QPI) + (r % QPI) * D;
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qop[s] = *reinterpret_cast<const bf16x8*>(qs + 8 * ((2 * s + hf) ^ (r & (CPR - 1))));
@@ -375,8 +383,9 @@ struct LargeTile {
   }
 };
 
-// One kernel for both cache types; FP8 selects the copy-and-widen staging.
-template <int D, int KB, bool FP8>
+// One kernel for both cache types; FP8 selects the copy-and-widen staging, C32
+// the 32-bit copy offsets (kv_copy_offset32; pools within its bounds).
+template <int D, int KB, bool FP8, bool C32>
 __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
   using LT = LargeTile<D, KB>;
   constexpr int TILE = LT::TILE, CPR = LT::CPR, NI = LT::NI;
@@ -408,19 +417,27 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
     const uint32_t kps = (uint32_t)(a.k_sp * 2), kbs = (uint32_t)(a.k_sb * 2);
     const uint32_t vps = (uint32_t)(a.v_sp * 2), vbs = (uint32_t)(a.v_sb * 2);
     // The copy of a block is NI load-to-LDS instructions per wave for K and NI for
-    // V; lane l of instruction i carries chunk q = (wave*NI + i)*64 + l of the
+    // V; lane l of instruction i carries chunk q = copy_chunk0(i) + l of the
     // block, i.e. block token q / CPR.  Each wave loads the page ids of its own
     // tokens one block ahead of the copy, so the addresses need no shared table.
     auto issue_copy = [&](auto& kd, auto& vd, int b, const int32_t (&raw)[NI]) {
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int q0 = (wave * NI + i) * 64;   // first LDS chunk of this instruction
+        const int q0 = t.copy_chunk0(i);   // first LDS chunk of this instruction
         const int q = q0 + lane;
         const int tk = q / CPR, j = q % CPR;
         const uint32_t page = (uint32_t)clamp_page(raw[i], a.num_pages);
         const int tok = t.template copy_token<CPR, NI>(b, i);
-        const char* gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, 16u * (j ^ kswz<D>(tk)));
-        const char* gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, 16u * (j ^ vswz<D>(tk)));
+        const uint32_t ik = 16u * (j ^ kswz<D>(tk)), iv = 16u * (j ^ vswz<D>(tk));
+        const char* gk;
+        const char* gv;
+        if constexpr (C32) {
+          gk = kbase + kv_copy_offset32(page, tok, a.log2B, kps, kbs, ik);
+          gv = vbase + kv_copy_offset32(page, tok, a.log2B, vps, vbs, iv);
+        } else {
+          gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, ik);
+          gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, iv);
+        }
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                          (__attribute__((address_space(3))) void*)(&kd[8 * q0]),
                                          16, 0, 0);
@@ -482,17 +499,24 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
     const char* vbase = static_cast<const char*>(a.v_cache) + (int64_t)it.hk * a.v_sh;
     const uint32_t kps = (uint32_t)a.k_sp, kbs = (uint32_t)a.k_sb;
     const uint32_t vps = (uint32_t)a.v_sp, vbs = (uint32_t)a.v_sb;
-    // lane l of copy instruction i carries chunk q = (wave*NI8 + i)*64 + l of the
+    // lane l of copy instruction i carries chunk q = copy_chunk0(i) + l of the
     // block (token q / CPR8), into the staging buffer as it sits in the cache row
     auto issue_copy8 = [&](uint8_t* kd, uint8_t* vd, int b, const int32_t (&raw)[NI8]) {
 #pragma unroll
       for (int i = 0; i < NI8; ++i) {
-        const int q0 = (wave * NI8 + i) * 64;   // first staging chunk of this instruction
+        const int q0 = t.copy_chunk0(i);   // first staging chunk of this instruction
         const int j = (q0 + lane) % CPR8;
         const uint32_t page = (uint32_t)clamp_page(raw[i], a.num_pages);
         const int tok = t.template copy_token<CPR8, NI8>(b, i);
-        const char* gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, 16u * j);
-        const char* gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, 16u * j);
+        const char* gk;
+        const char* gv;
+        if constexpr (C32) {
+          gk = kbase + kv_copy_offset32(page, tok, a.log2B, kps, kbs, 16u * j);
+          gv = vbase + kv_copy_offset32(page, tok, a.log2B, vps, vbs, 16u * j);
+        } else {
+          gk = kbase + kv_copy_offset(page, tok, a.log2B, kps, kbs, 16u * j);
+          gv = vbase + kv_copy_offset(page, tok, a.log2B, vps, vbs, 16u * j);
+        }
         __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(gk),
                                          (__attribute__((address_space(3))) void*)(&kd[16 * q0]),
                                          16, 0, 0);
@@ -565,17 +589,28 @@ hipError_t launch_attn_large(const AttnArgs& a, int n_items, int D, int kv_dtype
   (void)hipGetLastError();   // a stale error of an earlier call is not this launch's
   if (n_items <= 0) return hipSuccess;
   dim3 grid((unsigned)n_items);
+  const int eb = kv_dtype == AK_FP8_E4M3 ? 1 : 2;
+  const bool c32 = kv_copy32_ok(a.num_pages, a.k_sp * eb, a.k_sb * eb, 1 << a.log2B, (int64_t)D * eb) &&
+                   kv_copy32_ok(a.num_pages, a.v_sp * eb, a.v_sb * eb, 1 << a.log2B, (int64_t)D * eb);
+#define AK_LARGE(DD, F8)                                                                          \
+  do {                                                                                            \
+    if (c32)                                                                                      \
+      hipLaunchKernelGGL((attn_large_kernel<DD, kDmaKB, F8, true>), grid, dim3(512), 0, s, a);   \
+    else                                                                                          \
+      hipLaunchKernelGGL((attn_large_kernel<DD, kDmaKB, F8, false>), grid, dim3(512), 0, s, a);  \
+  } while (0)
   if (D == 128 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<128, kDmaKB, false>), grid, dim3(512), 0, s, a);
+    AK_LARGE(128, false);
   } else if (D == 64 && kv_dtype == AK_BF16) {
-    hipLaunchKernelGGL((attn_large_kernel<64, kDmaKB, false>), grid, dim3(512), 0, s, a);
+    AK_LARGE(64, false);
   } else if (D == 128 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<128, kDmaKB, true>), grid, dim3(512), 0, s, a);
+    AK_LARGE(128, true);
   } else if (D == 64 && kv_dtype == AK_FP8_E4M3) {
-    hipLaunchKernelGGL((attn_large_kernel<64, kDmaKB, true>), grid, dim3(512), 0, s, a);
+    AK_LARGE(64, true);
   } else {
     return hipErrorInvalidValue;
   }
+#undef AK_LARGE
   return hipGetLastError();
 }
 

@@ -22,7 +22,7 @@ struct StoreArgs {
 hipError_t launch_store_kv(const StoreArgs& a, int src_dtype, int dst_dtype, hipStream_t s);
 
 // addressing: 0 = the decode / fp32 kernels' row offsets, 1 = the prefill
-// kernels' copy offsets
+// kernels' copy offsets, 2 = their 32-bit form (page ids below 2^24)
 hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int32_t* kv_indices,
                                int32_t R, int32_t log2B, int64_t num_pages, int32_t addressing,
                                int64_t* slots, hipStream_t s);
@@ -85,6 +85,27 @@ __device__ __forceinline__ uint64_t kv_copy_offset(uint32_t page, int32_t t, int
                                                    uint32_t in_row) {
   const uint32_t slot = (uint32_t)(t & ((1 << log2B) - 1));
   return (uint64_t)page * page_stride + (slot * slot_stride + in_row);
+}
+
+// The same offset formed entirely in 32 bits with 24-bit multiplies, for pools
+// that satisfy kv_copy32_ok: every page id below 2^24, page and slot strides
+// below 2^24 bytes and the whole pool (from the head's base) within 4 GiB, so
+// the address is a uniform 64-bit base plus this per-lane 32-bit offset.
+__device__ __forceinline__ uint32_t kv_copy_offset32(uint32_t page, int32_t t, int32_t log2B,
+                                                     uint32_t page_stride, uint32_t slot_stride,
+                                                     uint32_t in_row) {
+  const uint32_t slot = (uint32_t)(t & ((1 << log2B) - 1));
+  return __umul24(page, page_stride) + __umul24(slot, slot_stride) + in_row;
+}
+
+// Host check for kv_copy_offset32: num_pages pages of page_stride bytes with
+// slots of slot_stride bytes (B per page) and rows of row_bytes.
+inline bool kv_copy32_ok(int64_t num_pages, int64_t page_stride, int64_t slot_stride, int32_t B,
+                         int64_t row_bytes) {
+  constexpr int64_t k24 = int64_t(1) << 24;
+  if (num_pages < 1 || num_pages > k24 || page_stride >= k24 || slot_stride >= k24) return false;
+  const int64_t span = (num_pages - 1) * page_stride + (int64_t)(B - 1) * slot_stride + row_bytes;
+  return span <= (int64_t(1) << 32) - 1;
 }
 
 }  // namespace ak

@@ -1113,8 +1113,9 @@ extern "C" ak_status ak_plan_workgroups(const ak_plan_t* p, int32_t* wg_first, i
 extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int32_t addressing, int64_t* slots,
                                      void* stream) {
   if (!p || !slots) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: null argument");
-  if (addressing != 0 && addressing != 1)
-    return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: addressing must be 0 (decode) or 1 (prefill)");
+  if (addressing < 0 || addressing > 2)
+    return fail(AK_ERR_INVALID_ARG,
+                "ak_gather_slots: addressing must be 0 (decode), 1 (prefill) or 2 (prefill, 32-bit)");
   if (p->host_only) return fail(AK_ERR_INVALID_ARG, "ak_gather_slots: plan was built host-only");
   if (p->R == 0) return AK_OK;
   std::vector<int64_t> off(p->R, 0);
@@ -1130,8 +1131,8 @@ extern "C" ak_status ak_gather_slots(const ak_plan_t* p, int32_t addressing, int
   if (e != hipSuccess) return hip_fail(e, "ak_gather_slots: hipMalloc");
   e = hipMemcpyAsync(d_off, off.data(), off.size() * sizeof(int64_t), hipMemcpyHostToDevice, s);
   if (e == hipSuccess)
-    e = launch_gather_slots(p->d_reqs, d_off, p->kv_indices, p->R, p->log2B, INT32_MAX, addressing,
-                            slots, s);
+    e = launch_gather_slots(p->d_reqs, d_off, p->kv_indices, p->R, p->log2B,
+                            addressing == 2 ? (int64_t(1) << 24) : INT32_MAX, addressing, slots, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   (void)hipFree(d_off);
   if (e != hipSuccess) return hip_fail(e, "ak_gather_slots");

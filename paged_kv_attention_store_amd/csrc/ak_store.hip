@@ -154,11 +154,16 @@ __global__ __launch_bounds__(256) void gather_slots_kernel(const Req* __restrict
       // decode and fp32 kernels: clamped page id, then the row offset
       const int32_t page = kv_page_id(kv_indices, rq.page_off, t, log2B, num_pages);
       slots[base + t] = kv_row_offset(page, t, log2B, B, 1);
-    } else {
+    } else if (ADDRESSING == 1) {
       // prefill kernels: raw page id loaded ahead, clamped at the copy, copy offset
       const int32_t raw = kv_indices[kv_page_index(rq.page_off, t, log2B)];
       slots[base + t] = (int64_t)kv_copy_offset((uint32_t)clamp_page(raw, num_pages), t, log2B,
                                                 (uint32_t)B, 1u, 0u);
+    } else {
+      // prefill kernels on pools within kv_copy_offset32's bounds: the same, in 32 bits
+      const int32_t raw = kv_indices[kv_page_index(rq.page_off, t, log2B)];
+      slots[base + t] = (int64_t)kv_copy_offset32((uint32_t)clamp_page(raw, num_pages), t, log2B,
+                                                  (uint32_t)B, 1u, 0u);
     }
   }
 }
@@ -212,8 +217,11 @@ hipError_t launch_gather_slots(const Req* reqs, const int64_t* kv_off, const int
   if (addressing == 0) {
     hipLaunchKernelGGL(gather_slots_kernel<0>, grid, dim3(256), 0, s, reqs, kv_off, kv_indices,
                        log2B, num_pages, slots);
-  } else {
+  } else if (addressing == 1) {
     hipLaunchKernelGGL(gather_slots_kernel<1>, grid, dim3(256), 0, s, reqs, kv_off, kv_indices,
+                       log2B, num_pages, slots);
+  } else {
+    hipLaunchKernelGGL(gather_slots_kernel<2>, grid, dim3(256), 0, s, reqs, kv_off, kv_indices,
                        log2B, num_pages, slots);
   }
   return hipGetLastError();

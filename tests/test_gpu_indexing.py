@@ -13,7 +13,8 @@ from tests.gpu_harness import plan_for, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("addressing", [0, 1], ids=["decode_rows", "prefill_copies"])
+@pytest.mark.parametrize("addressing", [0, 1, 2], ids=["decode_rows", "prefill_copies",
+                                                      "prefill_copies32"])
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5])
 def test_gather_slots_bit_exact(k, addressing):
     # the slots come from the kernels' own K/V addressing functions (page-id read,
@@ -41,7 +42,8 @@ INDEX_EDGE = [
 ]
 
 
-@pytest.mark.parametrize("addressing", [0, 1], ids=["decode_rows", "prefill_copies"])
+@pytest.mark.parametrize("addressing", [0, 1, 2], ids=["decode_rows", "prefill_copies",
+                                                      "prefill_copies32"])
 @pytest.mark.parametrize("case", INDEX_EDGE, ids=[c[0] for c in INDEX_EDGE])
 def test_gather_slots_edge_geometries(case, addressing):
     name, ql, kl, B = case

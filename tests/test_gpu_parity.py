@@ -271,6 +271,39 @@ def test_strided_views(kd):
             assert torch.all(torch.isnan(lse_wide[:, 1::2]))
 
 
+@pytest.mark.parametrize("kd", ["bf16", "fp8"])
+def test_prefill_copies_with_64bit_offsets(kd):
+    # The prefill kernels form their copy addresses in 32 bits when the pool's
+    # page stride, page count and span allow it; a page stride of 2^24 bytes (the
+    # caches as views into a wider buffer) takes the 64-bit form instead.
+    wl = W.custom(seed=23, q_lens=[90, 1, 130, 70], kv_lens=[300, 40, 700, 70], page_size=64,
+                  num_qo_heads=16, num_kv_heads=4, head_dim=128, kv_dtype=kd, windows=(-1, 100),
+                  name=f"copy64_{kd}")
+    say(f"[layout] prefill copies with 64-bit offsets, {kd} caches")
+    d = prepare(wl)
+    P, B, H, D = d["k_cache"].shape
+    eb = d["k_cache"].element_size()
+    sp = (1 << 24) // eb                     # page stride of 2^24 bytes, in elements
+    views = []
+    for c in (d["k_cache"], d["v_cache"]):
+        buf = torch.zeros(P * sp, dtype=c.dtype, device="cuda")
+        v = buf.as_strided((P, B, H, D), (sp, H * D, D, 1))
+        v.copy_(c)
+        views.append(v)
+    for window in wl.windows:
+        plan = plan_for(wl, d, window)
+        assert ak.ak_plan_info(plan)["large_items"] > 0
+        out = torch.full_like(d["q"], float("nan"))
+        lse = torch.full((wl.total_q, wl.num_qo_heads), float("nan"), device="cuda")
+        ak.ak_run(plan, d["q"], views[0], views[1], out=out, lse=lse, k_scale=wl.kv_scale,
+                  v_scale=wl.kv_scale)
+        torch.cuda.synchronize()
+        check(wl, out, lse, window)
+        # the same bits as the 32-bit form on the compact caches
+        o2, l2 = run(wl, d, plan)
+        assert torch.equal(out, o2) and torch.equal(lse, l2)
+
+
 def test_page_table_span_forces_more_splits():
     # page size 1 and at most 2 splits: a part may not span more than the 1024
     # pages a small tile stages, so the planner cuts more parts than max_splits
