@@ -30,6 +30,7 @@ namespace ak {
 namespace {
 
 constexpr float kLazy = 8.0f;    // raise the running max only beyond this margin (base 2)
+constexpr float kLazyP = 256.0f; // 2^kLazy
 constexpr int kDmaKB = 128;      // tokens per KV block
 constexpr int kLgkmcntZero = 0xC07F;   // s_waitcnt lgkmcnt(0), other counters unconstrained
 
@@ -221,13 +222,49 @@ struct LargeTile {
       pop[kh] = __builtin_bit_cast(bf16x8, pw);
     }
   }
+  // Fast-path tile: probabilities against the current reference max first; only
+  // if some lane's partial sum exceeds 2^kLazy (so one of its probabilities might)
+  // or there is no reference yet is the tile max taken, the reference raised by the
+  // same rule as tile_max / raise_max and the probabilities recomputed.  A sum
+  // within the bound means every probability is, i.e. the tile max does not exceed
+  // the reference by kLazy: the same decision without the max.
+  __device__ __forceinline__ void exp_sum(const f32x16& sacc, float (&p)[16], float& psum) const {
+    const float msub = m_run == -INFINITY ? 0.f : m_run;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) p[i] = fast_exp2(__builtin_fmaf(sacc[i], c, -msub));
+    psum = p[0];
+#pragma unroll
+    for (int i = 1; i < 16; ++i) psum += p[i];
+  }
+  __device__ __forceinline__ void exp_check_pack(const f32x16& sacc, bf16x8 (&pop)[2]) {
+    float p[16];
+    float psum;
+    exp_sum(sacc, p, psum);
+    if (__any((psum > kLazyP) | (m_run == -INFINITY))) {
+      raise_max(tile_max(sacc));
+      exp_sum(sacc, p, psum);
+    }
+    l_run += psum;
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      u32x4 pw;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) pw[h] = pack_bf16x2(p[8 * kh + 2 * h], p[8 * kh + 2 * h + 1]);
+      pop[kh] = __builtin_bit_cast(bf16x8, pw);
+    }
+  }
   __device__ __forceinline__ void o_mfma(const bf16x8 (&vop)[NDT], const bf16x8& pop) {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) oacc[dt] = mfma32(vop[dt], pop, oacc[dt]);
   }
 
   // attention of the wave's rows over the block whose first KV position is tb,
-  // held in the compute tiles kc / vc
+  // held in the compute tiles kc / vc.  LATE_MAX: the fast path forms each tile's
+  // probabilities before (and usually instead of) its max (exp_check_pack); else
+  // the max of tile T+1 is taken beside the PV MFMAs of tile T.  (Both keep the
+  // same reference-max rule; the fp8 staging, whose block starts with the widening
+  // pass, schedules better with the max first.)
+  template <bool LATE_MAX>
   __device__ __forceinline__ void compute(const __bf16 (&kc)[TILE], const __bf16 (&vc)[TILE], int tb) {
     bf16x8 kop[NS];
     bf16x8 vop[NDT];
@@ -239,7 +276,7 @@ struct LargeTile {
       read_k(kc, 0, kop);
       f32x16 sa = s_mfma(kop);
       if (NT > 1) read_k(kc, 1, kop);
-      raise_max(tile_max(sa));
+      if constexpr (!LATE_MAX) raise_max(tile_max(sa));
 #pragma unroll
       for (int T = 0; T < NT; ++T) {
         read_v(vc, 2 * T, vop);
@@ -248,14 +285,22 @@ struct LargeTile {
           sb = s_mfma(kop);
           if (T + 2 < NT) read_k(kc, T + 2, kop);
         }
-        exp_pack(sa, pop);
-        o_mfma(vop, pop[0]);
-        read_v(vc, 2 * T + 1, vop);
-        const float m_next = T + 1 < NT ? tile_max(sb) : 0.f;
-        o_mfma(vop, pop[1]);
-        if (T + 1 < NT) {
-          raise_max(m_next);
-          sa = sb;
+        if constexpr (LATE_MAX) {
+          exp_check_pack(sa, pop);
+          o_mfma(vop, pop[0]);
+          read_v(vc, 2 * T + 1, vop);
+          o_mfma(vop, pop[1]);
+          if (T + 1 < NT) sa = sb;
+        } else {
+          exp_pack(sa, pop);
+          o_mfma(vop, pop[0]);
+          read_v(vc, 2 * T + 1, vop);
+          const float m_next = T + 1 < NT ? tile_max(sb) : 0.f;
+          o_mfma(vop, pop[1]);
+          if (T + 1 < NT) {
+            raise_max(m_next);
+            sa = sb;
+          }
         }
       }
     } else {
@@ -452,7 +497,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
     auto step = [&](int b, auto& kc, auto& vc, auto& kn, auto& vn) {
       if (b + 1 < nb) issue_copy(kn, vn, b + 1, raw);
       if (b + 2 < nb) t.template load_pages<CPR, NI>(b + 2, raw);
-      if (t.wave_active) t.compute(kc, vc, it.kv_begin + b * KB);
+      if (t.wave_active) t.template compute<true>(kc, vc, it.kv_begin + b * KB);
       __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
       __syncthreads();
     };
@@ -552,7 +597,7 @@ __global__ __launch_bounds__(512, 2) void attn_large_kernel(AttnArgs a) {
       if (b + 2 < nb) t.template load_pages<CPR8, NI8>(b + 2, raw);
       widen(kc8, vc8);
       __syncthreads();                            // the widened block is complete
-      if (t.wave_active) t.compute(kb, vb, it.kv_begin + b * KB);
+      if (t.wave_active) t.template compute<false>(kb, vb, it.kv_begin + b * KB);
       __builtin_amdgcn_s_waitcnt(0);              // this wave's copies have landed
       __syncthreads();                            // and no wave still reads kb / vb
     };
