@@ -19,6 +19,7 @@ constexpr int kSmallMaxPages = 1024;  // pages a small-tile item may span (its L
 constexpr int kLargeTile = 32;    // KV tokens per tile of the large-tile cost model
 constexpr int kBlockTiles = 4;    // tiles per KV block of the large-tile kernel (split boundary)
 constexpr int kSegCost = 3;       // start-up cost of a large-tile segment, in tiles
+constexpr int kXcds = 8;          // dies (XCDs) of the chip, each with its own L2
 constexpr int kMinPartTiles = 8;  // smallest KV part a large tile job is split into, in tiles
 constexpr double kTileBytes = 4.0e6;  // bytes the whole GPU streams in one large-tile time
 constexpr int kPartsPerCu = 6;    // decode KV parts per compute unit the split aims at
@@ -74,6 +75,9 @@ struct ak_plan_t {
   float sm_scale = 0.f;
   int64_t T = 0;
   int32_t num_cus = 256;
+  // dies the large-tile segments are grouped by (1: longest first only); fixed
+  // plans keep 1, since the grouping pads the work list beyond their capacity
+  int32_t xcds = 1;
   bool host_only = false;
   std::vector<int32_t> kv_lens;
   std::vector<ak::Req> reqs;

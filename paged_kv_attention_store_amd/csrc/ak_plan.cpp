@@ -436,9 +436,76 @@ ak_status build_plan_host(const int32_t* qo_indptr, const int32_t* kv_indptr,
     for (size_t k = 0; k < segs.size(); ++k) order[k] = (int32_t)k;
     std::stable_sort(order.begin(), order.end(),
                      [&](int32_t x, int32_t y) { return segs[(size_t)x].cost > segs[(size_t)y].cost; });
+    // The dispatcher hands workgroups to the chip's X dies in turn (workgroup x to
+    // die x mod X), and each die has its own L2.  The segments of one (request, KV
+    // head) read the same K/V rows, so they are kept on one die: each unit, cut
+    // into pieces of at most half a die's share of the work, goes (longest piece
+    // first) to the least-loaded die; each die's segments keep the longest-first
+    // order; the dies' lists are interleaved, shorter ones padded with empty items
+    // (zero rows, which a workgroup leaves at once).  Only for batches of few
+    // units (at most two per die, e.g. one long chunk's KV heads): there each
+    // unit's segments would otherwise fetch its K/V once per die (measured: 305
+    // against 56 MB per launch on a 2048-token chunk, same time); with many units
+    // the grouping cut no traffic and its coarser balance cost about 1%.
+    const int X = p->xcds;
+    size_t units = 0;
+    for (size_t i = 0; i < nj; ++i)
+      if (i == 0 || jobs[i].r != jobs[i - 1].r || jobs[i].hk != jobs[i - 1].hk) ++units;
+    if (X > 1 && segs.size() > (size_t)X && units <= 2 * (size_t)X) {
+      int64_t total_cost = 0;
+      for (const Seg& g : segs) total_cost += g.cost;
+      const int64_t cap = std::max<int64_t>(1, total_cost / (2 * X));
+      // pieces: runs of consecutive segments of one unit (segments are in job
+      // order, jobs in (request, KV head, first row) order)
+      std::vector<int32_t> piece_of(segs.size());
+      std::vector<int64_t> piece_cost;
+      for (size_t k = 0; k < segs.size(); ++k) {
+        const Item& jk = jobs[(size_t)segs[k].job];
+        bool same = false;
+        if (k > 0) {
+          const Item& jp = jobs[(size_t)segs[k - 1].job];
+          same = jp.r == jk.r && jp.hk == jk.hk && piece_cost.back() + segs[k].cost <= cap;
+        }
+        if (!same) piece_cost.push_back(0);
+        piece_of[k] = (int32_t)piece_cost.size() - 1;
+        piece_cost.back() += segs[k].cost;
+      }
+      std::vector<int32_t> porder(piece_cost.size());
+      for (size_t k = 0; k < porder.size(); ++k) porder[k] = (int32_t)k;
+      std::stable_sort(porder.begin(), porder.end(), [&](int32_t x, int32_t y) {
+        return piece_cost[(size_t)x] > piece_cost[(size_t)y];
+      });
+      std::vector<int64_t> load((size_t)X, 0);
+      std::vector<int32_t> die_of(piece_cost.size());
+      for (int32_t pc : porder) {
+        const size_t d = (size_t)(std::min_element(load.begin(), load.end()) - load.begin());
+        die_of[(size_t)pc] = (int32_t)d;
+        load[d] += piece_cost[(size_t)pc];
+      }
+      std::vector<std::vector<int32_t>> dies((size_t)X);
+      for (int32_t k : order) dies[(size_t)die_of[(size_t)piece_of[(size_t)k]]].push_back(k);
+      size_t longest_list = 0;
+      for (const auto& d : dies) longest_list = std::max(longest_list, d.size());
+      std::vector<int32_t> inter;
+      inter.reserve(longest_list * (size_t)X);
+      for (size_t i = 0; i < longest_list; ++i)
+        for (int d = 0; d < X; ++d) inter.push_back(i < dies[(size_t)d].size() ? dies[(size_t)d][i] : -1);
+      while (!inter.empty() && inter.back() < 0) inter.pop_back();
+      order.swap(inter);
+    }
     std::vector<Item> sorted;
     sorted.reserve(order.size());
-    for (int32_t k : order) sorted.push_back(p->large_items[(size_t)k]);
+    for (int32_t k : order) {
+      if (k >= 0) {
+        sorted.push_back(p->large_items[(size_t)k]);
+      } else {
+        Item pad{};
+        pad.kind = 1;
+        pad.pbase = -1;
+        pad.merge0 = -1;
+        sorted.push_back(pad);
+      }
+    }
     p->large_items.swap(sorted);
   }
   p->partial_rows = prow;

@@ -383,6 +383,7 @@ extern "C" ak_status ak_plan(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (cus == 0) cus = device_cus(dev);
   }
   if (cus == 0) cus = 256;
+  p->xcds = kXcds;
   ak_status st;
   try {
     st = build_plan_host(qo_indptr, kv_indptr, last_page_len, batch_size, num_qo_heads,
@@ -982,6 +983,7 @@ extern "C" ak_status ak_run_noalloc(const int32_t* qo_indptr, const int32_t* kv_
   auto* p = new_plan();
   if (!p) return fail(AK_ERR_OOM, "ak_run_noalloc: out of host memory");
   const int cus = opts && opts->num_cus > 0 ? opts->num_cus : device_cus(dev);
+  p->xcds = kXcds;
   try {
     st = build_plan_host(qo_indptr, kv_indptr, last_page_len, batch_size, num_qo_heads,
                          num_kv_heads, head_dim, page_size, causal, window, opts, cus, p);

@@ -113,6 +113,10 @@ def check_coverage(qo, kv, last, B, hq, hkv, causal, window, **kw):
     cover = {}
     partial_rows = set()
     for r, hk, row0, nrows, kb, ke, pbase, kind in items.tolist():
+        if nrows == 0:
+            # an empty item (padding between the dies' lists of large segments)
+            assert kind == 1 and kb == ke == 0 and pbase == -1
+            continue
         assert 0 <= kb <= ke <= Ls[r]
         assert kind == (0 if ns[r] * G <= 16 else 1)
         key = (r, hk)
@@ -251,6 +255,18 @@ def _cost(large):
     return np.ceil((large[:, 5] - large[:, 4]) / 32.0)
 
 
+XCDS = 8   # dies of the chip: workgroup x runs on die x mod 8
+
+
+def _die_lists(large):
+    """The live large items each die runs, in dispatch order."""
+    out = []
+    for d in range(XCDS):
+        sub = large[d::XCDS]
+        out.append(sub[sub[:, 3] > 0])
+    return out
+
+
 def test_large_tiles_longest_first_without_splits():
     # many jobs against 256 compute units: no job exceeds the per-unit share, so
     # nothing is split; the dispatch order is longest KV range first
@@ -279,8 +295,10 @@ def test_large_split_of_few_long_jobs(seed):
     P = int(rng.choice([16, 64, 256]))
     p, _ = check_coverage(qo, kv, last, B, 8, 2, True, -1, num_cus=P)
     large, info = _large(p)
-    c = _cost(large)
-    assert np.all(np.diff(c) <= 0)
+    # few units: grouped by die, each die's list longest first
+    for lst in _die_lists(large):
+        assert np.all(np.diff(_cost(lst)) <= 0)
+    large = large[large[:, 3] > 0]
     split = large[large[:, 6] >= 0]
     assert len(split) > 0
     # parts of one job share (request, head, rows) and tile its KV range
@@ -291,6 +309,31 @@ def test_large_split_of_few_long_jobs(seed):
         assert len(parts) >= 2
         n_merge += key[3]
     assert info["small_items"] == 0 and n_merge == info["merge_jobs"]
+
+
+def test_few_units_grouped_by_die():
+    # one 2048-token chunk over a 6144-token prefix, 8 KV heads: 8 units of 32
+    # segments.  Each unit's segments read the same K/V rows, so all of them run on
+    # one die (one L2); the dies' lists are interleaved in dispatch order.
+    qo = np.array([0, 2048])
+    L = 8192
+    B = 64
+    kv = np.array([0, L // B])
+    last = np.array([B])
+    p, _ = check_coverage(qo, kv, last, B, 32, 8, True, -1, num_cus=256)
+    large, info = _large(p)
+    lists = _die_lists(large)
+    for d, lst in enumerate(lists):
+        assert len(lst) == 32
+        assert len({(r, hk) for r, hk in lst[:, :2].tolist()}) == 1
+        assert np.all(np.diff(_cost(lst)) <= 0)
+    assert len({tuple(lst[0, :2]) for lst in lists}) == 8
+    # many units (the ragged prefill batch): no grouping, longest first overall
+    wl = W.config(3)
+    p = host_plan(wl.qo_indptr, wl.kv_indptr, wl.last_page_len, hq=wl.num_qo_heads,
+                  hkv=wl.num_kv_heads, B=wl.page_size, causal=True, window=-1, num_cus=256)
+    large, _ = _large(p)
+    assert np.all(large[:, 3] > 0) and np.all(np.diff(_cost(large)) <= 0)
 
 
 # ------------------------------------------------------- non-causal segments
