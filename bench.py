@@ -332,6 +332,18 @@ def _host_cores():
     return cpus, blas
 
 
+def _cpu_model():
+    """The host CPU's model name, as the kernel reports it."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def _cpu_leg(wl, reqs, budget_s, what):
     """Time the float64 oracle on `reqs` of `wl` (full attention) until `budget_s`
     seconds of passes; its algorithmic work in the GPU metric's unit."""
@@ -385,7 +397,7 @@ def cpu_baseline(k, wl=None):
     for what, rr, b in legs:
         value, unit, tok_s, passes, t = _cpu_leg(wl, rr, b, what)
         out.append({"value": round(value, 4), "unit": unit, "cores": int(blas), "host_cpus": cpus,
-                    "kind": "oracle", "phase": what,
+                    "cpu_model": _cpu_model(), "kind": "oracle", "phase": what,
                     "tokens_per_s": round(tok_s, 2), "wall_s_per_pass": round(t / passes, 3),
                     "sample": f"{wl.name}: {desc}; {what} part: requests {rr[:4]}"
                               f"{'...' if len(rr) > 4 else ''}, one layer, {passes} passes in "
