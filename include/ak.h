@@ -422,7 +422,10 @@ ak_status ak_plan_workgroups(const ak_plan_t* plan, int32_t* wg_first, int64_t c
  * Each item is 8 int32: request, kv_head, first row, row count, kv_begin,
  * kv_end, partial base (-1 = writes the output directly), kind (0 small tile,
  * 1 large tile).  Row rho of (request r, KV head hk) is query token
- * qo_indptr[r] + rho / G and query head hk*G + rho % G.  Also writes the
+ * qo_indptr[r] + rho / G and query head hk*G + rho % G.  Items are in launch
+ * order (small items first); the large items of an ordinary plan with few
+ * units are grouped by die and may include empty items (row count 0, kind 1,
+ * partial base -1) that hold a dispatch slot and do nothing.  Also writes the
  * per-request KV lengths L_r into `kv_lens` (host int32 [batch_size], may be
  * NULL).  `items` holds `capacity` items; more than that returns
  * AK_ERR_INVALID_ARG with the needed count in *count. */
