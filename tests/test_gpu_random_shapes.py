@@ -86,3 +86,75 @@ def test_random_batch_parity(seed):
             plan = plan_for(wl, d, window, **kw)
             out, lse = run(wl, d, plan)
             check(wl, out, lse, window)
+
+
+# Longer batches: extend chunks of up to 1536 tokens on prefixes of up to 3000, so
+# a (request, KV head) spans several 256-row segments and many 128-token KV blocks
+# (the reference max raised inside long block runs, segments grouped by die when
+# the batch has few units, KV splits of long segments); page sizes up to 128.
+# Compared on sampled rows: the first and last three of each request and 26 drawn.
+LONG_SEEDS = list(range(12))
+
+
+def draw_long(seed: int):
+    rng = np.random.default_rng(8100 + seed)
+    R = int(rng.integers(1, 5))
+    B = int(rng.choice([1, 2, 16, 64, 128]))
+    hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
+    D = int(rng.choice([64, 128]))
+    kd = "fp8" if rng.random() < 0.4 else "bf16"
+    causal = bool(rng.random() < 0.85)
+    q_lens, kv_lens = [], []
+    for _ in range(R):
+        q = 1 if rng.random() < 0.2 else int(rng.integers(65, 1537))
+        prefix = int(rng.integers(0, 3001))
+        q_lens.append(q)
+        kv_lens.append(q + prefix)
+    windows = (-1, int(rng.integers(64, 2049))) if causal and rng.random() < 0.5 else (-1,)
+    split = {"min_chunk": 128, "num_cus": int(rng.choice([64, 1024])),
+             "merge_in_kernel": bool(rng.random() < 0.5)}
+    name = f"long{seed}_B{B}_h{hq}x{hkv}_D{D}_{kd}_{'c' if causal else 'nc'}"
+    wl = W.custom(seed=9500 + seed, q_lens=q_lens, kv_lens=kv_lens, page_size=B,
+                  num_qo_heads=hq, num_kv_heads=hkv, head_dim=D, q_dtype="bf16", kv_dtype=kd,
+                  causal=causal, windows=windows, name=name)
+    return wl, windows, split
+
+
+def _sampled_rows(wl, seed):
+    rng = np.random.default_rng(8200 + seed)
+    rows = {}
+    for r in range(wl.batch_size):
+        n = int(wl.q_lens[r])
+        pick = set(range(min(3, n))) | set(range(max(0, n - 3), n))
+        pick |= set(rng.integers(0, n, size=min(26, n)).tolist()) if n else set()
+        rows[r] = sorted(pick)
+    return rows
+
+
+@pytest.mark.parametrize("seed", LONG_SEEDS)
+def test_long_random_batch_plans_on_host(seed):
+    wl, windows, split = draw_long(seed)
+    for window in windows:
+        for kw in ({}, split):
+            plan = ak.ak_plan(wl.qo_indptr, wl.kv_indptr, None, wl.last_page_len,
+                              wl.num_qo_heads, wl.num_kv_heads, wl.head_dim, wl.page_size,
+                              causal=wl.causal, window=window, host_only=True, **kw)
+            info = ak.ak_plan_info(plan)
+            assert info["batch_size"] == wl.batch_size and info["total_q"] == wl.total_q
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", LONG_SEEDS)
+def test_long_random_batch_parity(seed):
+    from tests.gpu_harness import check, plan_for, prepare, run, say
+
+    wl, windows, split = draw_long(seed)
+    say(f"[random-long] {wl.name} q={wl.q_lens.tolist()} kv={wl.kv_lens.tolist()} "
+        f"windows={windows} split={split}")
+    rows = _sampled_rows(wl, seed)
+    d = prepare(wl)
+    for window in windows:
+        for kw in ({}, split):
+            plan = plan_for(wl, d, window, **kw)
+            out, lse = run(wl, d, plan)
+            check(wl, out, lse, window, rows_of=lambda r: rows[r])
